@@ -1,0 +1,200 @@
+"""Decode-step benchmark of the paged KV-cache hot path on one MI355X.
+
+A step is one decode iteration of one attention layer over the whole batch:
+the step's cache writes (copy-on-write block copies, then the append of the
+new tokens' K/V into their slots) followed by paged decode attention.  The
+default workload is the Llama-3-8B-shaped GQA layer: 128 sequences, 32 query
+/ 8 KV heads of 128, bf16, 16-token blocks, contexts log-uniform in
+[256, 8192], shuffled physical pool.  Inputs are seeded and synthetic and are
+resident in HBM before timing starts.
+
+Prints ONE JSON line.  ``value`` is the KV bytes a step reads (each cached
+token's K and V once) divided by the measured step time, in GB/s.
+``roofline`` prices the attention kernels (partition + merge, launched by one
+paged_attention_decode call) against MI355X's 8 TB/s HBM peak, with their
+duration measured by HIP events on the launching stream.  ``cpu_baseline``
+times the CPU oracle on the same step's inputs.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from paged_kv_cache_388_amd import workloads as wl  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) and seqs/s"
+
+
+def algorithmic_bytes(w):
+    """Bytes paged_attention_decode must move for one call: every context
+    token's K and V once, q in, out back, the block ids and context lengths."""
+    b = wl.ELEM_BYTES[w.dtype]
+    ids = sum((int(n) + w.block_size - 1) // w.block_size for n in w.context_lens)
+    return (w.kv_bytes() + 2 * w.num_seqs * w.num_q_heads * w.head_dim * b + 4 * ids
+            + 4 * w.num_seqs)
+
+
+def cpu_baseline(w, max_seconds):
+    """The fp64 oracle on this step's inputs, single-threaded (BLAS pinned to
+    one thread): append into the host pools, then attention over as many
+    sequences as fit in about ``max_seconds``.  Rate in KV GB/s of the
+    sequences it finished."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        kc, vc = w.k_cache, w.v_cache
+        if len(w.block_mapping):
+            kc, vc = oracle.copy_blocks(kc, vc, w.block_mapping)
+        if len(w.slot_mapping):
+            kc, vc = oracle.kv_append(kc, vc, w.new_key, w.new_value, w.slot_mapping)
+        done = []
+        for s in range(w.num_seqs):
+            oracle.decode_attention(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                                    w.dtype, seq_ids=[s])
+            done.append(s)
+            if time.perf_counter() - t0 > max_seconds:
+                break
+        dt = time.perf_counter() - t0
+    b = wl.ELEM_BYTES[w.dtype]
+    kv = 2 * int(w.context_lens[done].astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * b
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{len(done)} of {w.num_seqs} sequences of the same step "
+                       f"(append + attention), fp64 NumPy, {dt:.1f} s"),
+            "seqs_per_s": len(done) / dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3_8b_gqa",
+                    help="one of: " + ", ".join(wl.NAMED[:4]) + ", long_ctx_bs16, long_ctx_bs32")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="bound on the CPU oracle baseline (0 disables it)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    t_gen = time.perf_counter()
+    w = wl.named(args.workload)
+    print(f"[bench] workload {w.name} generated in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        print(f"[bench] cpu oracle: {cpu['sample']}", file=sys.stderr, flush=True)
+
+    import torch
+    from paged_kv_cache_388_amd import _lib
+    _lib.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.int32 or w.dtype == "f32":
+            return torch.from_numpy(a).to(dev)
+        tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(tdt)
+
+    q = up(w.q)
+    k_cache, v_cache = up(w.k_cache), up(w.v_cache)
+    block_tables, context_lens = up(w.block_tables), up(w.context_lens)
+    block_mapping = up(w.block_mapping.astype(np.int32))
+    slot_mapping = up(w.slot_mapping.astype(np.int32))
+    new_key, new_value = up(w.new_key), up(w.new_value)
+    out = torch.empty_like(q)
+    ws_bytes = _lib.paged_attention_workspace_bytes(w.num_seqs, w.num_q_heads, w.head_dim,
+                                                    w.max_context_len)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    max_ctx = w.max_context_len
+    torch.cuda.synchronize()
+
+    def write_step():
+        if block_mapping.shape[0]:
+            _lib.paged_copy_blocks(k_cache, v_cache, block_mapping)
+        if slot_mapping.shape[0]:
+            _lib.paged_kv_append(new_key, new_value, k_cache, v_cache, slot_mapping)
+
+    def attend():
+        _lib.paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
+                                    w.scale, max_ctx, workspace)
+
+    for _ in range(args.warmup):
+        write_step()
+        attend()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        write_step()
+        starts[i].record(stream)
+        attend()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    attn_avg_ms = float(np.mean(attn_ms))
+    kv = w.kv_bytes()
+    value = kv / (ms_per_step * 1e-3) / 1e9
+    alg = algorithmic_bytes(w)
+    achieved = alg / (attn_avg_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "num_blocks": w.num_blocks,
+                   "mean_context": round(float(w.context_lens.mean()), 1),
+                   "max_context": max_ctx, "kv_bytes_per_step": kv, "seed": w.seed,
+                   "step": "copy_blocks + paged_kv_append + paged_attention_decode",
+                   "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "seqs_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
+        "attention_ms": {"mean": round(attn_avg_ms, 4),
+                         "p10": round(float(np.percentile(attn_ms, 10)), 4),
+                         "p50": round(float(np.percentile(attn_ms, 50)), 4),
+                         "p90": round(float(np.percentile(attn_ms, 90)), 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None,
+                     "kernel": "attn_partition_kernel + attn_reduce_kernel (one decode call)",
+                     "algorithmic_bytes_per_launch": alg},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,173 @@
+/*
+ * libpagedkv — paged KV-cache decode for AMD Instinct MI355X (gfx950).
+ *
+ * The KV cache of one attention layer lives in a shared pool of fixed-size
+ * physical blocks; each sequence owns a block table that maps its logical
+ * blocks to physical ones, so its context is contiguous logically but
+ * scattered physically.  Sources: "Optimizing LLM Inference: From
+ * PagedAttention to AI Infra" (sections "PagedAttention: Decoupling Logical
+ * Context from Contiguous GPU Memory", "On-Demand Allocation", "Copy-on-Write");
+ * "The Memory Wall" (sections "How it Works Under the Hood", "Show Me The
+ * Code: A Conceptual PagedAttention Kernel"); "05 PagedAttention" (sections
+ * "How PagedAttention Works (vLLM)", "KV Cache Sharing (Copy-on-Write)").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pool layout, K and V alike: [num_blocks, num_kv_heads, block_size,
+ *    head_dim], row-major, elements of the pool's dtype.  One (block, head)
+ *    tile of block_size x head_dim elements is contiguous.
+ *  - dtype is one of pkv_dtype; every tensor passed to one call shares it.
+ *  - All pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates and frees nothing.  Pointers must be 16-byte aligned.
+ *  - Calls are asynchronous on `stream` (0 = the null stream): they validate
+ *    their scalar arguments on the host, enqueue kernels and return.  Inputs
+ *    must stay valid and unmodified until the stream reaches the work.
+ *  - Host-side validation failures return PKV_EINVAL / PKV_EUNSUPPORTED and
+ *    enqueue nothing; a failed launch returns PKV_EHIP.  pkv_last_error()
+ *    then holds a message (per calling thread).
+ *  - Device-side metadata (block ids, context lengths, slots) is trusted for
+ *    correctness but never for memory safety: a block id or slot outside the
+ *    pool is skipped instead of dereferenced, and a context length is clamped
+ *    to [0, max_context_len].
+ *  - Thread safety: the library keeps no mutable global state apart from the
+ *    per-thread error message.  Calls on different streams may overlap.
+ */
+#ifndef PAGEDKV_H_
+#define PAGEDKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_API __attribute__((visibility("default")))
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,        /* bad pointer, shape or scalar argument */
+  PKV_EUNSUPPORTED = 2,  /* valid but not built: head_dim, block_size, dtype, group */
+  PKV_EWORKSPACE = 3,    /* workspace missing or smaller than required */
+  PKV_EHIP = 4,          /* a HIP runtime call or kernel launch failed */
+  PKV_ECHECK = 5         /* reserved for metadata validation failures */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+/* Shape of the K and V pools (they share it). */
+typedef struct {
+  int32_t num_blocks;    /* physical blocks in the pool, > 0 */
+  int32_t num_kv_heads;  /* H_kv, > 0 */
+  int32_t block_size;    /* tokens per block: 16 or 32 */
+  int32_t head_dim;      /* D: 64 or 128 */
+  int32_t dtype;         /* pkv_dtype */
+} pkv_pool;
+
+/* Tokens per split-context partition of paged_attention_decode (512). */
+PKV_API int32_t pkv_partition_tokens(void);
+
+/*
+ * paged_kv_append — write new tokens' K and V into their cache slots
+ * ("On-Demand Allocation" on the first page: a sequence's newest tokens go
+ * into the next free slots of its blocks; "How it Works Under the Hood" on
+ * "The Memory Wall": the model writes a logically contiguous sequence).
+ *
+ *   key, value    [num_tokens, num_kv_heads, head_dim]  contiguous, pool dtype
+ *   k_cache, v_cache  pools (see above), written in place
+ *   slot_mapping  [num_tokens] int32: slot = physical_block * block_size + offset;
+ *                 a negative slot or one >= num_blocks * block_size is skipped.
+ *                 Two tokens naming the same slot in one call race (undefined).
+ *   num_tokens    >= 0 (0 enqueues nothing)
+ * Every element is a raw bit copy.  Returns PKV_OK once enqueued.
+ */
+PKV_API pkv_status paged_kv_append(const void* key, const void* value,
+                                   void* k_cache, void* v_cache, pkv_pool pool,
+                                   const int32_t* slot_mapping, int32_t num_tokens,
+                                   hipStream_t stream);
+
+/*
+ * Bytes of workspace paged_attention_decode needs for this shape: fp32
+ * partial states of every (sequence, query head, partition) when a context
+ * can span more than one partition, else 0.  Returns 0 for invalid input.
+ */
+PKV_API size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t head_dim, int32_t max_context_len);
+
+/*
+ * paged_attention_decode — one query token per sequence attends to its whole
+ * cached context, gathered block by block through its block table (first
+ * page, "PagedAttention: Decoupling Logical Context from Contiguous GPU
+ * Memory"; "The Memory Wall", "Show Me The Code: A Conceptual PagedAttention
+ * Kernel").  For sequence s and query head h, with n = context_lens[s] and
+ * G = num_q_heads / num_kv_heads, query head h reads KV head h / G:
+ *
+ *     out[s, h, :] = softmax_t(scale * q[s, h, :] . K_s[h/G, t, :]) @ V_s[h/G, t, :]
+ *
+ * over logical tokens t < n; token t lives in physical block
+ * block_tables[s, t / block_size] at offset t % block_size.  n = 0 gives a
+ * zero row.  Softmax and accumulation are fp32; out is rounded to nearest
+ * even in the pool dtype.  Contexts longer than one partition are split into
+ * partitions computed independently and merged exactly (log-sum-exp rescale);
+ * the order of every reduction depends only on logical positions, so the
+ * result is bit-identical under any physical placement of the blocks.
+ *
+ *   out           [num_seqs, num_q_heads, head_dim]  pool dtype, written
+ *   q             [num_seqs, num_q_heads, head_dim]  pool dtype
+ *   k_cache, v_cache  pools, read only
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32; entries at
+ *                 j >= ceil(n / block_size) are never read
+ *   context_lens  [num_seqs] int32, each <= max_context_len
+ *   num_q_heads   multiple of num_kv_heads, with G = num_q_heads/num_kv_heads <= 16
+ *   scale         logit scale, usually 1/sqrt(head_dim)
+ *   max_context_len  host-known upper bound of context_lens (no device read);
+ *                 max_blocks_per_seq * block_size must be >= it
+ *   workspace     device buffer of >= paged_attention_workspace_bytes(...)
+ *                 bytes (may be NULL when that is 0); contents are scratch
+ */
+PKV_API pkv_status paged_attention_decode(void* out, const void* q,
+                                          const void* k_cache, const void* v_cache,
+                                          pkv_pool pool,
+                                          const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens,
+                                          int32_t num_seqs, int32_t num_q_heads,
+                                          float scale, int32_t max_context_len,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+
+/*
+ * paged_copy_blocks — copy-on-write block duplication ("05 PagedAttention",
+ * "KV Cache Sharing (Copy-on-Write)": a sequence that diverges gets its own
+ * copy of a shared block while the shared block stays as it was).  For each
+ * pair i, block block_mapping[2i] is copied to block block_mapping[2i+1],
+ * every KV head of K and of V, as raw bits.
+ *
+ *   block_mapping [num_pairs, 2] int32 (src, dst) on the device.  Destinations
+ *                 must be distinct and no destination may be a source in the
+ *                 same call (else the result depends on scheduling).  Pairs
+ *                 naming a block outside the pool are skipped.
+ */
+PKV_API pkv_status paged_copy_blocks(void* k_cache, void* v_cache, pkv_pool pool,
+                                     const int32_t* block_mapping, int32_t num_pairs,
+                                     hipStream_t stream);
+
+/*
+ * pkv_stream_copy — plain device-to-device copy of `bytes` bytes (a multiple
+ * of 16) with 16-byte vector loads and stores.  A bandwidth and counter
+ * reference for the kernels above, not part of the attention method.
+ */
+PKV_API pkv_status pkv_stream_copy(void* dst, const void* src, size_t bytes,
+                                   hipStream_t stream);
+
+PKV_API const char* pkv_status_string(pkv_status status);
+/* Message of the calling thread's last failed call ("" if none). */
+PKV_API const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H_ */

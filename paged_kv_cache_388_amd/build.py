@@ -1,0 +1,64 @@
+"""Build libpagedkv.so in-tree with hipcc for gfx950.
+
+    python -m paged_kv_cache_388_amd.build          # or build() from Python
+
+Every HIP source is compiled with packed-fp32 instruction selection disabled
+(scalar and float2 fp32 code is then issued as ordinary VALU ops).
+"""
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OUT = os.path.join(PKG, "libpagedkv.so")
+OBJDIR = os.path.join(ROOT, "_build")
+
+SOURCES = ["attention.hip", "cache_ops.hip", "pagedkv_api.cpp"]
+ARCH = "gfx950"
+
+
+def hipcc():
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def compile_flags():
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-fvisibility=hidden", f"-I{INCLUDE}", f"-I{CSRC}",
+            "-Wno-unused-command-line-argument"]
+
+
+def _compile(src):
+    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *compile_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    return obj
+
+
+def build(verbose=False):
+    """Compile every source and link libpagedkv.so next to this file."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = OUT + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, OUT)
+    if verbose:
+        print(f"built {OUT}")
+    return OUT
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

@@ -1,0 +1,108 @@
+// Cache writes for gfx950: append of new tokens into their slots, copy-on-write
+// block duplication, and a plain streaming copy used as a bandwidth and
+// counter reference.  All three are raw 16-byte bit copies.
+//
+// Append: a sequence's newest tokens go into free slots of its blocks as they
+// arrive ("Optimizing LLM Inference: From PagedAttention to AI Infra", section
+// "On-Demand Allocation"; "The Memory Wall", "How it Works Under the Hood").
+// The slot encodes block * block_size + offset.
+// Copy: a writer to a shared block first gets a private copy while the shared
+// block stays unchanged ("05 PagedAttention", "KV Cache Sharing
+// (Copy-on-Write)"; first page, "Copy-on-Write").
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kThreads = 256;
+
+// One thread per 16-byte chunk of one token's [H_kv, D] row, for K and V.
+// Consecutive threads cover consecutive chunks of a head, so reads of the
+// input rows are fully coalesced and each (head, slot) destination row of
+// D * elem_bytes bytes is written contiguously.
+__global__ __launch_bounds__(kThreads) void kv_append_kernel(
+    const uint4* __restrict__ key, const uint4* __restrict__ value, char* __restrict__ k_cache,
+    char* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping, int32_t num_tokens,
+    int32_t chunks_per_head, int32_t num_kv_heads, int32_t block_size, int64_t num_slots) {
+  const int64_t per_token = (int64_t)chunks_per_head * num_kv_heads;
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (gid >= per_token * num_tokens) return;
+  const int64_t i = gid / per_token;
+  const int64_t rem = gid - i * per_token;
+  const int32_t slot = slot_mapping[i];
+  if (slot < 0 || (int64_t)slot >= num_slots) return;
+  const int64_t blk = slot / block_size;
+  const int64_t off = slot - blk * block_size;
+  const int64_t h = rem / chunks_per_head;
+  const int64_t c = rem - h * chunks_per_head;
+  const int64_t dst = (((blk * num_kv_heads + h) * block_size + off) * chunks_per_head + c) * 16;
+  reinterpret_cast<uint4*>(k_cache + dst)[0] = key[gid];
+  reinterpret_cast<uint4*>(v_cache + dst)[0] = value[gid];
+}
+
+// One workgroup per (pair, K or V): copies a whole block of every KV head.
+__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
+    char* __restrict__ k_cache, char* __restrict__ v_cache, const int32_t* __restrict__ block_mapping,
+    int64_t block_chunks, int32_t num_blocks) {
+  const int pair = blockIdx.x >> 1;
+  char* pool = (blockIdx.x & 1) ? v_cache : k_cache;
+  const int32_t src = block_mapping[2 * pair];
+  const int32_t dst = block_mapping[2 * pair + 1];
+  if ((unsigned)src >= (unsigned)num_blocks || (unsigned)dst >= (unsigned)num_blocks) return;
+  const uint4* from = reinterpret_cast<const uint4*>(pool + (int64_t)src * block_chunks * 16);
+  uint4* to = reinterpret_cast<uint4*>(pool + (int64_t)dst * block_chunks * 16);
+  for (int64_t c = threadIdx.x; c < block_chunks; c += kThreads) to[c] = from[c];
+}
+
+__global__ __launch_bounds__(kThreads) void stream_copy_kernel(uint4* __restrict__ dst,
+                                                               const uint4* __restrict__ src,
+                                                               int64_t chunks) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < chunks; c += stride)
+    dst[c] = src[c];
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const void* key, const void* value, void* k_cache, void* v_cache,
+                            const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                            int32_t block_size, int32_t head_dim, int32_t elem_bytes,
+                            int32_t num_blocks, hipStream_t stream) {
+  if (num_tokens <= 0) return hipSuccess;
+  const int32_t chunks_per_head = head_dim * elem_bytes / 16;
+  const int64_t total = (int64_t)chunks_per_head * num_kv_heads * num_tokens;
+  const int64_t nwg = (total + kThreads - 1) / kThreads;
+  if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)nwg), dim3(kThreads), 0, stream,
+                     static_cast<const uint4*>(key), static_cast<const uint4*>(value),
+                     static_cast<char*>(k_cache), static_cast<char*>(v_cache), slot_mapping,
+                     num_tokens, chunks_per_head, num_kv_heads, block_size,
+                     (int64_t)num_blocks * block_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
+                              int32_t num_pairs, size_t block_bytes, int32_t num_blocks,
+                              hipStream_t stream) {
+  if (num_pairs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs * 2u), dim3(kThreads), 0, stream,
+                     static_cast<char*>(k_cache), static_cast<char*>(v_cache), block_mapping,
+                     (int64_t)(block_bytes / 16), num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  const int64_t chunks = (int64_t)(bytes / 16);
+  if (chunks == 0) return hipSuccess;
+  int64_t nwg = (chunks + kThreads - 1) / kThreads;
+  if (nwg > 256 * 64) nwg = 256 * 64;  // grid-stride beyond 64 workgroups per CU
+  hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)nwg), dim3(kThreads), 0, stream,
+                     static_cast<uint4*>(dst), static_cast<const uint4*>(src), chunks);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

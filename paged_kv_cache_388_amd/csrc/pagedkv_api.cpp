@@ -1,0 +1,188 @@
+// C ABI of libpagedkv: host-side argument validation and kernel dispatch.
+// Declarations and the contract of every entry point: include/pagedkv.h.
+
+#include "pagedkv.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pkv_status hip_fail(hipError_t err, const char* what) {
+  return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_F16:
+    case PKV_BF16: return 2;
+    default: return 0;
+  }
+}
+
+pkv_status check_pool(const pkv_pool& pool) {
+  if (elem_bytes(pool.dtype) == 0) return fail(PKV_EUNSUPPORTED, "dtype %d is not f32/f16/bf16", pool.dtype);
+  if (pool.num_blocks <= 0 || pool.num_kv_heads <= 0)
+    return fail(PKV_EINVAL, "pool needs num_blocks > 0 and num_kv_heads > 0 (got %d, %d)",
+                pool.num_blocks, pool.num_kv_heads);
+  if (pool.block_size != 16 && pool.block_size != 32)
+    return fail(PKV_EUNSUPPORTED, "block_size %d is not 16 or 32", pool.block_size);
+  if (pool.head_dim != 64 && pool.head_dim != 128)
+    return fail(PKV_EUNSUPPORTED, "head_dim %d is not 64 or 128", pool.head_dim);
+  return PKV_OK;
+}
+
+size_t pool_block_bytes(const pkv_pool& pool) {
+  return (size_t)pool.num_kv_heads * pool.block_size * pool.head_dim * elem_bytes(pool.dtype);
+}
+
+int32_t partitions_for(int32_t max_context_len) {
+  const int32_t P = (max_context_len + pkv::kPartitionTokens - 1) / pkv::kPartitionTokens;
+  return P > 0 ? P : 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_partition_tokens(void) { return pkv::kPartitionTokens; }
+
+const char* pkv_status_string(pkv_status status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_EINVAL: return "invalid argument";
+    case PKV_EUNSUPPORTED: return "unsupported configuration";
+    case PKV_EWORKSPACE: return "workspace missing or too small";
+    case PKV_EHIP: return "HIP runtime error";
+    case PKV_ECHECK: return "metadata check failed";
+  }
+  return "unknown status";
+}
+
+const char* pkv_last_error(void) { return g_err; }
+
+pkv_status paged_kv_append(const void* key, const void* value, void* k_cache, void* v_cache,
+                           pkv_pool pool, const int32_t* slot_mapping, int32_t num_tokens,
+                           hipStream_t stream) {
+  g_err[0] = '\0';
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens %d < 0", num_tokens);
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(PKV_EINVAL, "null pointer argument");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_EINVAL, "key, value and the pools must be 16-byte aligned");
+  if ((long long)pool.num_blocks * pool.block_size > 0x7fffffffLL)
+    return fail(PKV_EINVAL, "num_blocks * block_size exceeds the int32 slot range");
+  hipError_t err = pkv::launch_kv_append(key, value, k_cache, v_cache, slot_mapping, num_tokens,
+                                         pool.num_kv_heads, pool.block_size, pool.head_dim,
+                                         elem_bytes(pool.dtype), pool.num_blocks, stream);
+  return err == hipSuccess ? PKV_OK : hip_fail(err, "paged_kv_append launch");
+}
+
+size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                       int32_t max_context_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  const int32_t P = partitions_for(max_context_len);
+  if (P <= 1) return 0;
+  return (size_t)num_seqs * num_q_heads * P * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+pkv_status paged_attention_decode(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, pkv_pool pool,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, float scale, int32_t max_context_len,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = '\0';
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs %d < 0", num_seqs);
+  if (num_seqs == 0) return PKV_OK;
+  if (num_q_heads <= 0 || num_q_heads % pool.num_kv_heads != 0)
+    return fail(PKV_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, pool.num_kv_heads);
+  const int32_t group = num_q_heads / pool.num_kv_heads;
+  if (group > 16) return fail(PKV_EUNSUPPORTED, "query heads per kv head %d > 16", group);
+  if (max_context_len < 0) return fail(PKV_EINVAL, "max_context_len %d < 0", max_context_len);
+  if (max_blocks_per_seq < 0 || (long long)max_blocks_per_seq * pool.block_size < max_context_len)
+    return fail(PKV_EINVAL, "max_blocks_per_seq %d * block_size %d < max_context_len %d",
+                max_blocks_per_seq, pool.block_size, max_context_len);
+  if (!(scale == scale)) return fail(PKV_EINVAL, "scale is NaN");
+  if (!out || !q || !k_cache || !v_cache || !context_lens || (max_blocks_per_seq > 0 && !block_tables))
+    return fail(PKV_EINVAL, "null pointer argument");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_EINVAL, "out, q and the pools must be 16-byte aligned");
+  const size_t need = paged_attention_workspace_bytes(num_seqs, num_q_heads, pool.head_dim,
+                                                      max_context_len);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (need > 0 && !aligned16(workspace)) return fail(PKV_EINVAL, "workspace must be 16-byte aligned");
+
+  pkv::AttnParams prm;
+  prm.out = out;
+  prm.q = q;
+  prm.k_cache = k_cache;
+  prm.v_cache = v_cache;
+  prm.block_tables = block_tables;
+  prm.context_lens = context_lens;
+  prm.max_blocks_per_seq = max_blocks_per_seq;
+  prm.num_seqs = num_seqs;
+  prm.num_q_heads = num_q_heads;
+  prm.num_kv_heads = pool.num_kv_heads;
+  prm.group = group;
+  prm.num_blocks = pool.num_blocks;
+  prm.max_context_len = max_context_len;
+  prm.max_partitions = partitions_for(max_context_len);
+  prm.scale_log2 = scale * 1.4426950408889634f;
+  const size_t po = (size_t)num_seqs * num_q_heads * prm.max_partitions * pool.head_dim;
+  prm.part_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  prm.part_ml = need > 0 ? static_cast<float*>(workspace) + po : nullptr;
+  hipError_t err = pkv::launch_paged_attention(prm, pool.dtype, pool.head_dim, pool.block_size, stream);
+  return err == hipSuccess ? PKV_OK : hip_fail(err, "paged_attention_decode launch");
+}
+
+pkv_status paged_copy_blocks(void* k_cache, void* v_cache, pkv_pool pool,
+                             const int32_t* block_mapping, int32_t num_pairs, hipStream_t stream) {
+  g_err[0] = '\0';
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return fail(PKV_EINVAL, "num_pairs %d < 0", num_pairs);
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !block_mapping) return fail(PKV_EINVAL, "null pointer argument");
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return fail(PKV_EINVAL, "pools must be 16-byte aligned");
+  if (num_pairs > 0x3fffffff) return fail(PKV_EINVAL, "num_pairs %d too large", num_pairs);
+  hipError_t err = pkv::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs,
+                                           pool_block_bytes(pool), pool.num_blocks, stream);
+  return err == hipSuccess ? PKV_OK : hip_fail(err, "paged_copy_blocks launch");
+}
+
+pkv_status pkv_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (bytes == 0) return PKV_OK;
+  if (!dst || !src) return fail(PKV_EINVAL, "null pointer argument");
+  if (!aligned16(dst) || !aligned16(src) || (bytes & 15u))
+    return fail(PKV_EINVAL, "pointers and byte count must be multiples of 16");
+  hipError_t err = pkv::launch_stream_copy(dst, src, bytes, stream);
+  return err == hipSuccess ? PKV_OK : hip_fail(err, "pkv_stream_copy launch");
+}
+
+}  // extern "C"
