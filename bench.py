@@ -73,6 +73,35 @@ def cpu_baseline(w, max_seconds):
             "seqs_per_s": len(done) / dt}
 
 
+def copy_probe(mib, steps, warmup):
+    """Time the library's plain 16-byte-vector copy: its duration gives the
+    achievable read+write rate, and its FETCH_SIZE / WRITE_SIZE counters per
+    dispatch calibrate the attention kernel's counters (known bytes moved)."""
+    import torch
+    from paged_kv_cache_388_amd import _lib
+    _lib.load()
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        _lib.pkv_stream_copy(dst, src)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        a[i].record(stream)
+        _lib.pkv_stream_copy(dst, src)
+        b[i].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([x.elapsed_time(y) for x, y in zip(a, b)]))
+    assert torch.equal(dst, src)
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
+                      "ms_per_copy": round(ms, 4),
+                      "read_plus_write_GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,12 +111,19 @@ def main():
                     help="one of: " + ", ".join(wl.NAMED[:4]) + ", long_ctx_bs16, long_ctx_bs32")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="bound on the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the decode step, time pkv_stream_copy of this many MiB "
+                         "(the reference copy for bandwidth and HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib, args.steps, args.warmup)
+        return
 
     t_gen = time.perf_counter()
     w = wl.named(args.workload)
