@@ -102,6 +102,32 @@ def copy_probe(mib, steps, warmup):
                       "read_plus_write_GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
 
 
+def read_probe(mib, steps, warmup):
+    """Time the library's plain streaming read: the achievable read rate that
+    the decode kernel's bandwidth is compared with."""
+    import torch
+    from paged_kv_cache_388_amd import _lib
+    _lib.load()
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.random_(0, 255)
+    sink = torch.zeros(_lib.STREAM_READ_WORKGROUPS, dtype=torch.int32, device="cuda")
+    for _ in range(warmup):
+        _lib.pkv_stream_read(src, sink)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        a[i].record(stream)
+        _lib.pkv_stream_read(src, sink)
+        b[i].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([x.elapsed_time(y) for x, y in zip(a, b)]))
+    print(json.dumps({"read_probe_bytes": n, "ms_per_read": round(ms, 4),
+                      "read_GBps": round(n / (ms * 1e-3) / 1e9, 1)}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +137,9 @@ def main():
                     help="one of: " + ", ".join(wl.NAMED[:4]) + ", long_ctx_bs16, long_ctx_bs32")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="bound on the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--read-probe-mib", type=int, default=0,
+                    help="instead of the decode step, time pkv_stream_read of this many MiB "
+                         "(the achievable read-bandwidth reference)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the decode step, time pkv_stream_copy of this many MiB "
                          "(the reference copy for bandwidth and HBM counter calibration)")
@@ -123,6 +152,9 @@ def main():
 
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib, args.steps, args.warmup)
+        return
+    if args.read_probe_mib > 0:
+        read_probe(args.read_probe_mib, args.steps, args.warmup)
         return
 
     t_gen = time.perf_counter()

@@ -162,6 +162,15 @@ PKV_API pkv_status paged_copy_blocks(void* k_cache, void* v_cache, pkv_pool pool
 PKV_API pkv_status pkv_stream_copy(void* dst, const void* src, size_t bytes,
                                    hipStream_t stream);
 
+/*
+ * pkv_stream_read — read `bytes` bytes (a multiple of 16) once with 16-byte
+ * vector loads; each of 2048 workgroups writes one XOR-fold word to
+ * sink[0..2047] (device, caller-owned).  The achievable-read-bandwidth
+ * reference for the decode kernel, not part of the attention method.
+ */
+PKV_API pkv_status pkv_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                                   hipStream_t stream);
+
 PKV_API const char* pkv_status_string(pkv_status status);
 /* Message of the calling thread's last failed call ("" if none). */
 PKV_API const char* pkv_last_error(void);

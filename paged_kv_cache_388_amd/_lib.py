@@ -57,6 +57,8 @@ def load():
     lib.paged_copy_blocks.restype = c_i32
     lib.pkv_stream_copy.argtypes = [c_vp, c_vp, c_sz, c_vp]
     lib.pkv_stream_copy.restype = c_i32
+    lib.pkv_stream_read.argtypes = [c_vp, c_sz, c_vp, c_vp]
+    lib.pkv_stream_read.restype = c_i32
     lib.pkv_status_string.argtypes = [c_i32]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_last_error.argtypes = []
@@ -182,3 +184,17 @@ def pkv_stream_copy(dst, src, stream=None):
     if dst.numel() * dst.element_size() != nbytes:
         raise ValueError("dst and src differ in size")
     _check(load().pkv_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)))
+
+
+STREAM_READ_WORKGROUPS = 2048
+
+
+def pkv_stream_read(src, sink, stream=None):
+    """Read every byte of src once; sink is an int32/uint32 device tensor of
+    at least 2048 elements that receives one XOR-fold word per workgroup."""
+    _need(src, "src")
+    _need(sink, "sink", device=src.device)
+    if sink.numel() * sink.element_size() < 4 * STREAM_READ_WORKGROUPS:
+        raise ValueError("sink must hold 2048 32-bit words")
+    _check(load().pkv_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                  _stream(stream)))

@@ -8,10 +8,10 @@
 // table lookup per block is the structure kept here).  Query head h reads KV
 // head h / G.
 //
-// Work decomposition.  One workgroup (4 waves) per (kv head, sequence,
-// 512-token partition); all G query heads of the kv head share the K/V bytes
-// it streams, so every K/V byte crosses HBM once per step.  Wave w takes the
-// partition's 16-token sub-tiles w, w+4, w+8, ...
+// Work unit.  One item = (kv head, sequence, 512-token partition), handled by
+// one workgroup of 4 waves; all G query heads of the kv head share the K/V
+// bytes it streams, so every K/V byte crosses HBM once per step.  Wave w takes
+// the item's 16-token sub-tiles w, w+4, w+8, ...
 //
 // Per 16-token sub-tile a wave does:
 //   QK   S^T[16 tok x 16 cols] = K_tile[16 x D] . Q^T[D x 16] on MFMA
@@ -25,12 +25,21 @@
 //        accumulator when the max grows.
 //   PV   O^T[D x 16] += V^T[D x 16 tok] . P^T[16 tok x 16] on MFMA
 //        (16x16x16).  P^T is the QK result already in place.  V^T is built
-//        from natural 16-byte V loads: the head-dim index d is permuted so that
-//        MFMA row rho, pass mm holds d = (D/16)*rho + mm, which makes each lane's
+//        from natural V loads: the head-dim index d is permuted so that MFMA
+//        row rho, pass mm holds d = (D/16)*rho + mm, which makes each lane's
 //        four token chunks the four k-values of its A operand (one v_perm_b32
 //        per pair).  P is split into hi + lo 16-bit parts so the product keeps
 //        ~16 mantissa bits instead of 8.
-// The reduction order depends only on logical token positions.
+// The reduction order depends only on logical token positions, never on
+// physical block ids or on which workgroup ran an item.
+//
+// Scheduling.  The persistent kernel launches two workgroups per CU.  Each
+// builds the dense list of non-empty items (prefix sum of partitions per
+// sequence, in LDS), takes a strided share of its XCD's contiguous range of
+// that list, and streams sub-tiles through a 3-deep register ring that runs
+// across item boundaries, with the next item's block ids and query prefetched
+// one item ahead.  The grid kernel (one workgroup per possible item) serves
+// batches too large for the LDS work list.
 //
 // Partitions: a context longer than 512 tokens is split into 512-token
 // partitions whose (max, normaliser, unnormalised output) are merged by a
@@ -56,6 +65,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSub = 16;  // tokens per MFMA row group
+constexpr int kXcds = 8;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
@@ -68,7 +78,6 @@ template <> struct Elem<DT_F32> { static constexpr int bytes = 4; };
 // head slowest): the sequences that read the same kv head's blocks, shared
 // prefixes included, then meet in the same L2.
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  constexpr int kXcds = 8;
   const int per = nblocks / kXcds, rem = nblocks % kXcds;
   const int xcd = bid % kXcds, local = bid / kXcds;
   const int start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
@@ -95,33 +104,58 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Raw buffer resource over one (block, head) tile: the base is uniform
+// (scalar registers), so a tile costs a few scalar ops plus two per-lane
+// offsets that never change.  Offsets at or past num_records read as zero
+// without touching memory.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit-dword buffer, gfx9 family
+// K and V bytes are read once per step: load them with the nontemporal cache
+// policy ("nt") so they stream through the caches instead of displacing
+// lines, which lifts sustained read bandwidth substantially on gfx950.
+constexpr int kStreamPolicy = 2;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_bytes, kRsrcWord3);
+}
+
 // One 16-token sub-tile in registers.  N = D * elem_bytes / 64.
-//   k[kk]   : token (lane & 15), 16-byte chunk (lane >> 4) + 4*kk of its row
+//   k[kk]   : bytes [1024*kk + 16*lane, +16) of the sub-tile (each load
+//             instruction reads 1 KiB of whole token rows)
 //   v[e][.] : token 4*(lane >> 4) + e, bytes [(lane & 15)*4N, +4N) of its row
+// Both patterns cover whole 128-byte lines per instruction, which the
+// nontemporal loads need to stream at full rate; a pattern that touches half
+// lines (16 rows x 64 bytes, the MFMA operand layout) runs ~15% slower.
 template <int N>
 struct Tile {
   uint4 k[N];
   uint32_t v[4][N];
 };
 
+// voff: this lane's V byte offset inside a 16-token sub-tile (K uses
+// 16*lane); soff: byte offset of the sub-tile inside its (block, head) tile.
 template <int N>
-__device__ __forceinline__ void load_tile(Tile<N>& t, const char* kbase, const char* vbase,
-                                          int lane) {
+__device__ __forceinline__ void load_tile(Tile<N>& t, rsrc_t kr, rsrc_t vr, int koff, int voff,
+                                          int soff) {
   constexpr int kRow = 16 * 4 * N;  // bytes per token row = D * elem_bytes
-  const int r = lane >> 4, c = lane & 15;
-  const char* kp = kbase + c * kRow + r * 16;
 #pragma unroll
-  for (int kk = 0; kk < N; ++kk) t.k[kk] = *reinterpret_cast<const uint4*>(kp + kk * 64);
-  const char* vp = vbase + (4 * r) * kRow + c * (4 * N);
+  for (int kk = 0; kk < N; ++kk)
+    t.k[kk] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + kk * 1024, soff, kStreamPolicy));
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if constexpr (N == 2) {
-      const uint2 x = *reinterpret_cast<const uint2*>(vp + e * kRow);
+      const uint2 x = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, voff + e * kRow, soff, kStreamPolicy));
       t.v[e][0] = x.x; t.v[e][1] = x.y;
     } else {
 #pragma unroll
       for (int j = 0; j < N / 4; ++j) {
-        const uint4 x = *reinterpret_cast<const uint4*>(vp + e * kRow + 16 * j);
+        const uint4 x = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + e * kRow + 16 * j, soff,
+                                                         kStreamPolicy));
         t.v[e][4 * j + 0] = x.x; t.v[e][4 * j + 1] = x.y;
         t.v[e][4 * j + 2] = x.z; t.v[e][4 * j + 3] = x.w;
       }
@@ -129,253 +163,229 @@ __device__ __forceinline__ void load_tile(Tile<N>& t, const char* kbase, const c
   }
 }
 
-template <int DT, int D, int BS>
-__global__ __launch_bounds__(kThreads) void attn_partition_kernel(AttnParams prm) {
-  constexpr int EB = Elem<DT>::bytes;
-  constexpr int N = D * EB / 64;           // 16-byte K chunks per lane per sub-tile
-  constexpr int kRow = D * EB;             // bytes per token row
-  constexpr int kMM = D / 16;              // PV passes (MFMA row blocks of the head dim)
-  static_assert(kPartitionTokens % BS == 0 && BS % kSub == 0, "partition/block sizes");
+// Query operand (B of the QK MFMA): lane (r, g) holds query head h*G+g,
+// 16-byte chunks r + 4*kk of its row; zero for padding columns.
+template <int N>
+__device__ __forceinline__ void load_query(uint4 (&qb)[N], const void* q, int s, int h, int G,
+                                           int Hq, int lane) {
+  constexpr int kRow = 64 * N;
+  const int r = lane >> 4, g = lane & 15;
+  const char* qrow = static_cast<const char*>(q) +
+                     ((size_t)s * Hq + (size_t)h * G + (g < G ? g : 0)) * kRow;
+#pragma unroll
+  for (int kk = 0; kk < N; ++kk)
+    qb[kk] = g < G ? *reinterpret_cast<const uint4*>(qrow + 16 * (r + 4 * kk)) : make_uint4(0, 0, 0, 0);
+}
 
-  __shared__ float sm_ml[kWaves][2][16];
-  __shared__ float sm_o[kWaves][16][D + 4];
-
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane >> 4;   // row group
-  const int g = lane & 15;   // MFMA column = query head within the group
-
-  const int P = prm.max_partitions;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int p = L % P;
-  const int sh = L / P;
-  const int s = sh % prm.num_seqs;
-  const int h = sh / prm.num_seqs;
-  const int G = prm.group;
-  const int Hq = prm.num_q_heads;
-
-  int ctx = prm.context_lens[s];
-  ctx = ctx < 0 ? 0 : (ctx > prm.max_context_len ? prm.max_context_len : ctx);
-  const int nparts = (ctx + kPartitionTokens - 1) / kPartitionTokens;
-  if (p >= (nparts > 0 ? nparts : 1)) return;
-  if (ctx == 0) {
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
-      store_out<DT>(prm.out, ((size_t)s * Hq + (size_t)h * G) * D + idx, 0.f);
-    return;
+// Per-wave online-softmax state of one item.
+template <int kMM>
+struct WaveState {
+  float m;           // running max of column (lane & 15), base-2 logits
+  float l;           // running normaliser of the lane's own tokens
+  floatx4 acc[kMM];  // O^T rows (D/16)*(4*(lane>>4)+rr) + mm, column lane & 15
+  __device__ __forceinline__ void reset() {
+    m = kNegInf;
+    l = 0.f;
+#pragma unroll
+    for (int mm = 0; mm < kMM; ++mm) acc[mm] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
+};
 
-  const int tok0 = p * kPartitionTokens;
-  const int ntok = min(kPartitionTokens, ctx - tok0);
-  const int nsub = (ntok + kSub - 1) / kSub;
-  const int niter = nsub > w ? (nsub - w + kWaves - 1) / kWaves : 0;
+// Re-deal a K sub-tile from its load order (lane-contiguous 16-byte chunks)
+// into the MFMA A operand order (lane l: token l & 15, chunks (l >> 4) + 4*kk)
+// through this wave's LDS slot.  Chunk c of token row t is stored at chunk
+// position c ^ (t & mask) so that both the writes and the 16-row reads spread
+// over the banks.
+template <int N>
+__device__ __forceinline__ void restage_k(uint4 (&a)[N], const Tile<N>& t, char* lds, int lane) {
+  constexpr int kRow = 64 * N;
+  constexpr int kSwz = (4 * N - 1) < 15 ? (4 * N - 1) : 15;
+#pragma unroll
+  for (int kk = 0; kk < N; ++kk) {
+    const int b = 1024 * kk + 16 * lane;
+    const int row = b / kRow, c = (b % kRow) / 16;
+    *reinterpret_cast<uint4*>(lds + row * kRow + ((c ^ (row & kSwz)) * 16)) = t.k[kk];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int row = lane & 15;
+#pragma unroll
+  for (int kk = 0; kk < N; ++kk) {
+    const int c = (lane >> 4) + 4 * kk;
+    a[kk] = *reinterpret_cast<const uint4*>(lds + row * kRow + ((c ^ (row & kSwz)) * 16));
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-  // Block ids of this wave's sub-tiles: lane i holds the id for iteration i.
-  const int32_t* bt_row = prm.block_tables + (size_t)s * prm.max_blocks_per_seq;
-  int my_id = 0;
-  if (lane < niter) my_id = bt_row[(tok0 + kSub * (w + kWaves * lane)) / BS];
-
-  // Query operand (B of the QK MFMA): lane (r, g) holds query head h*G+g,
-  // 16-byte chunks r + 4*kk of its row; zero for padding columns.
-  uint4 qb[N];
-  {
-    const char* qrow = static_cast<const char*>(prm.q) +
-                       (((size_t)s * Hq + (size_t)h * G + (g < G ? g : 0)) * D) * EB;
+// QK, mask, online softmax and PV of one 16-token sub-tile; `valid` tokens
+// (from the sub-tile's first) are real, the rest are masked.  `lds` is this
+// wave's private staging slot (at least one sub-tile of K).
+template <int DT, int N, int kMM>
+__device__ __forceinline__ void attend_subtile(Tile<N>& t, const uint4 (&qb)[N], int valid,
+                                               float scale_log2, int r, WaveState<kMM>& st,
+                                               char* lds) {
+  uint4 ka[N];
+  restage_k<N>(ka, t, lds, threadIdx.x & 63);
+  // ---- QK on MFMA ----------------------------------------------------------
+  floatx4 S = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (DT == DT_F32) {
 #pragma unroll
     for (int kk = 0; kk < N; ++kk) {
-      qb[kk] = g < G ? *reinterpret_cast<const uint4*>(qrow + 16 * (r + 4 * kk))
-                     : make_uint4(0, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(ka[kk].x), __uint_as_float(qb[kk].x), S, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(ka[kk].y), __uint_as_float(qb[kk].y), S, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(ka[kk].z), __uint_as_float(qb[kk].z), S, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(ka[kk].w), __uint_as_float(qb[kk].w), S, 0, 0, 0);
+    }
+  } else if constexpr (DT == DT_F16) {
+#pragma unroll
+    for (int kk = 0; kk < N; ++kk)
+      S = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, ka[kk]),
+                                                 __builtin_bit_cast(halfx8, qb[kk]), S, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < N; ++kk)
+      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kk]),
+                                                  __builtin_bit_cast(bf16x8, qb[kk]), S, 0, 0, 0);
+  }
+
+  // ---- mask + online softmax (lane (r, g) holds tokens 4r..4r+3 of column g)
+  float sv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) sv[e] = (4 * r + e < valid) ? S[e] * scale_log2 : kNegInf;
+  float mloc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  const float m_new = fmaxf(st.m, mloc);
+  const float mb = m_new == kNegInf ? 0.f : m_new;
+  const float alpha = fast_exp2(st.m - mb);
+  float pe[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(sv[e] - mb);
+  st.l = st.l * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
+  st.m = m_new;
+#pragma unroll
+  for (int mm = 0; mm < kMM; ++mm) st.acc[mm] *= alpha;
+
+  // ---- tail: V rows of masked tokens are zeroed (select, never 0 * v)
+  if (valid < kSub) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool keep = 4 * r + e < valid;
+#pragma unroll
+      for (int j = 0; j < N; ++j) t.v[e][j] = keep ? t.v[e][j] : 0u;
     }
   }
 
-  const size_t tile_bytes = (size_t)BS * kRow;                 // one (block, head) tile
-  const size_t block_bytes = tile_bytes * prm.num_kv_heads;
-  const char* kpool = static_cast<const char*>(prm.k_cache) + (size_t)h * tile_bytes;
-  const char* vpool = static_cast<const char*>(prm.v_cache) + (size_t)h * tile_bytes;
-  const float scale_log2 = prm.scale_log2;
-
-  float m_run = kNegInf;
-  float l_run = 0.f;
-  floatx4 acc[kMM];
+  // ---- PV on MFMA ----------------------------------------------------------
+  if constexpr (DT == DT_F32) {
 #pragma unroll
-  for (int mm = 0; mm < kMM; ++mm) acc[mm] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  auto tile_ptrs = [&](int i, const char*& kb, const char*& vb) {
-    int phys = __builtin_amdgcn_readlane(my_id, i);
-    if ((unsigned)phys >= (unsigned)prm.num_blocks) phys = 0;  // never dereference a bad id
-    const int off = (tok0 + kSub * (w + kWaves * i)) % BS;
-    const size_t o = (size_t)phys * block_bytes + (size_t)off * kRow;
-    kb = kpool + o;
-    vb = vpool + o;
-  };
-  auto issue = [&](Tile<N>& t, int i) {
-    const char *kb, *vb;
-    tile_ptrs(i, kb, vb);
-    load_tile<N>(t, kb, vb, lane);
-  };
-  auto compute = [&](Tile<N>& t, int i) {
-    const int tokb = tok0 + kSub * (w + kWaves * i);
-    const int phys = __builtin_amdgcn_readlane(my_id, i);
-    int valid = ctx - tokb;
-    valid = valid > kSub ? kSub : valid;
-    if ((unsigned)phys >= (unsigned)prm.num_blocks) valid = 0;
-
-    // ---- QK on MFMA --------------------------------------------------------
-    floatx4 S = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (DT == DT_F32) {
+    for (int mm = 0; mm < kMM; ++mm) {
 #pragma unroll
-      for (int kk = 0; kk < N; ++kk) {
-        S = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[kk].x), __uint_as_float(qb[kk].x), S, 0, 0, 0);
-        S = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[kk].y), __uint_as_float(qb[kk].y), S, 0, 0, 0);
-        S = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[kk].z), __uint_as_float(qb[kk].z), S, 0, 0, 0);
-        S = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[kk].w), __uint_as_float(qb[kk].w), S, 0, 0, 0);
-      }
-    } else if constexpr (DT == DT_F16) {
-#pragma unroll
-      for (int kk = 0; kk < N; ++kk)
-        S = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, t.k[kk]),
-                                                   __builtin_bit_cast(halfx8, qb[kk]), S, 0, 0, 0);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < N; ++kk)
-        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[kk]),
-                                                    __builtin_bit_cast(bf16x8, qb[kk]), S, 0, 0, 0);
+      for (int e = 0; e < 4; ++e)
+        st.acc[mm] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.v[e][mm]), pe[e],
+                                                          st.acc[mm], 0, 0, 0);
     }
-
-    // ---- mask + online softmax (lane (r, g) holds tokens 4r..4r+3 of column g)
-    float sv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sv[e] = (4 * r + e < valid) ? S[e] * scale_log2 : kNegInf;
-    float mloc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float mb = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - mb);
-    float pe[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(sv[e] - mb);
-    l_run = l_run * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
-    m_run = m_new;
-#pragma unroll
-    for (int mm = 0; mm < kMM; ++mm) acc[mm] *= alpha;
-
-    // ---- tail: V rows of masked tokens are zeroed (select, never 0 * v)
-    if (valid < kSub) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool keep = 4 * r + e < valid;
-#pragma unroll
-        for (int j = 0; j < N; ++j) t.v[e][j] = keep ? t.v[e][j] : 0u;
-      }
-    }
-
-    // ---- PV on MFMA ---------------------------------------------------------
-    if constexpr (DT == DT_F32) {
-#pragma unroll
-      for (int mm = 0; mm < kMM; ++mm) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[mm] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.v[e][mm]), pe[e], acc[mm], 0, 0, 0);
-      }
+  } else {
+    uint2 phi, plo;
+    if constexpr (DT == DT_BF16) {
+      // hi = truncation to bf16 (exact bits), lo = RNE(p - hi)
+      const uint32_t b0 = __float_as_uint(pe[0]), b1 = __float_as_uint(pe[1]);
+      const uint32_t b2 = __float_as_uint(pe[2]), b3 = __float_as_uint(pe[3]);
+      phi.x = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+      phi.y = __builtin_amdgcn_perm(b3, b2, 0x07060302u);
+      const floatx2 l01 = {pe[0] - __uint_as_float(b0 & 0xffff0000u),
+                           pe[1] - __uint_as_float(b1 & 0xffff0000u)};
+      const floatx2 l23 = {pe[2] - __uint_as_float(b2 & 0xffff0000u),
+                           pe[3] - __uint_as_float(b3 & 0xffff0000u)};
+      plo.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(l01, bf16x2));
+      plo.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(l23, bf16x2));
     } else {
-      uint2 phi, plo;
+      // hi = round-toward-zero to fp16, lo = the exact remainder rounded again
+      const fp16x2 h01 = __builtin_amdgcn_cvt_pkrtz(pe[0], pe[1]);
+      const fp16x2 h23 = __builtin_amdgcn_cvt_pkrtz(pe[2], pe[3]);
+      phi.x = __builtin_bit_cast(uint32_t, h01);
+      phi.y = __builtin_bit_cast(uint32_t, h23);
+      const fp16x2 l01 = __builtin_amdgcn_cvt_pkrtz(pe[0] - (float)h01[0], pe[1] - (float)h01[1]);
+      const fp16x2 l23 = __builtin_amdgcn_cvt_pkrtz(pe[2] - (float)h23[0], pe[3] - (float)h23[1]);
+      plo.x = __builtin_bit_cast(uint32_t, l01);
+      plo.y = __builtin_bit_cast(uint32_t, l23);
+    }
+#pragma unroll
+    for (int mm = 0; mm < kMM; ++mm) {
+      const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
+      const int wd = mm >> 1;
+      uint2 a;
+      a.x = __builtin_amdgcn_perm(t.v[1][wd], t.v[0][wd], sel);
+      a.y = __builtin_amdgcn_perm(t.v[3][wd], t.v[2][wd], sel);
       if constexpr (DT == DT_BF16) {
-        // hi = truncation to bf16 (exact bits), lo = RNE(p - hi)
-        const uint32_t b0 = __float_as_uint(pe[0]), b1 = __float_as_uint(pe[1]);
-        const uint32_t b2 = __float_as_uint(pe[2]), b3 = __float_as_uint(pe[3]);
-        phi.x = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
-        phi.y = __builtin_amdgcn_perm(b3, b2, 0x07060302u);
-        const floatx2 l01 = {pe[0] - __uint_as_float(b0 & 0xffff0000u),
-                             pe[1] - __uint_as_float(b1 & 0xffff0000u)};
-        const floatx2 l23 = {pe[2] - __uint_as_float(b2 & 0xffff0000u),
-                             pe[3] - __uint_as_float(b3 & 0xffff0000u)};
-        plo.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(l01, bf16x2));
-        plo.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(l23, bf16x2));
+        const shortx4 A = __builtin_bit_cast(shortx4, a);
+        st.acc[mm] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(shortx4, phi),
+                                                               st.acc[mm], 0, 0, 0);
+        st.acc[mm] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(shortx4, plo),
+                                                               st.acc[mm], 0, 0, 0);
       } else {
-        // hi = round-toward-zero to fp16, lo = the exact remainder rounded again
-        const fp16x2 h01 = __builtin_amdgcn_cvt_pkrtz(pe[0], pe[1]);
-        const fp16x2 h23 = __builtin_amdgcn_cvt_pkrtz(pe[2], pe[3]);
-        phi.x = __builtin_bit_cast(uint32_t, h01);
-        phi.y = __builtin_bit_cast(uint32_t, h23);
-        const fp16x2 l01 = __builtin_amdgcn_cvt_pkrtz(pe[0] - (float)h01[0], pe[1] - (float)h01[1]);
-        const fp16x2 l23 = __builtin_amdgcn_cvt_pkrtz(pe[2] - (float)h23[0], pe[3] - (float)h23[1]);
-        plo.x = __builtin_bit_cast(uint32_t, l01);
-        plo.y = __builtin_bit_cast(uint32_t, l23);
-      }
-#pragma unroll
-      for (int mm = 0; mm < kMM; ++mm) {
-        const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
-        const int wd = mm >> 1;
-        uint2 a;
-        a.x = __builtin_amdgcn_perm(t.v[1][wd], t.v[0][wd], sel);
-        a.y = __builtin_amdgcn_perm(t.v[3][wd], t.v[2][wd], sel);
-        if constexpr (DT == DT_BF16) {
-          const shortx4 A = __builtin_bit_cast(shortx4, a);
-          acc[mm] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(shortx4, phi),
-                                                              acc[mm], 0, 0, 0);
-          acc[mm] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(shortx4, plo),
-                                                              acc[mm], 0, 0, 0);
-        } else {
-          const halfx4 A = __builtin_bit_cast(halfx4, a);
-          acc[mm] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, __builtin_bit_cast(halfx4, phi),
-                                                          acc[mm], 0, 0, 0);
-          acc[mm] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, __builtin_bit_cast(halfx4, plo),
-                                                          acc[mm], 0, 0, 0);
-        }
+        const halfx4 A = __builtin_bit_cast(halfx4, a);
+        st.acc[mm] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, __builtin_bit_cast(halfx4, phi),
+                                                           st.acc[mm], 0, 0, 0);
+        st.acc[mm] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, __builtin_bit_cast(halfx4, plo),
+                                                           st.acc[mm], 0, 0, 0);
       }
     }
-  };
-
-  // Two register buffers: the next sub-tile's loads are in flight while the
-  // current one is computed.  Loads are issued unconditionally (the index is
-  // clamped to the last sub-tile) and the loop has a single exit, so the load
-  // counter waits the compiler derives stay per-buffer instead of draining the
-  // whole queue at the loop head.
-  if (niter > 0) {
-    Tile<N> ta, tb;
-    issue(ta, 0);
-    for (int i = 0; i + 1 < niter; i += 2) {
-      issue(tb, i + 1);
-      compute(ta, i);
-      issue(ta, i + 2 < niter ? i + 2 : niter - 1);
-      compute(tb, i + 1);
-    }
-    if (niter & 1) compute(ta, niter - 1);
   }
+}
 
-  // Column normaliser: sum over the four row groups.
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+// LDS used to merge the four waves' states of one item.  Between merges,
+// o[w] is wave w's private K staging slot (at least one 16-token sub-tile of
+// K: 16 * D * 4 bytes <= sizeof(o[w])).
+template <int D>
+struct MergeSmem {
+  float ml[kWaves][2][16];
+  float o[kWaves][16][D + 4];
+};
 
-  // ---- merge the four waves ------------------------------------------------
+// Merge the four waves' states of item (s, h, p) and write either the final
+// output (single-partition or empty context) or the partition's state.
+// Called by the whole workgroup; leaves the LDS free for the next item.
+template <int DT, int D, int kMM>
+__device__ __forceinline__ void merge_item(MergeSmem<D>& sm, WaveState<kMM>& st, const AttnParams& prm,
+                                           int w, int lane, int s, int h, int p, int nparts) {
+  const int r = lane >> 4, g = lane & 15;
+  const int G = prm.group;
+  // column normaliser: sum over the four row groups
+  st.l += __shfl_xor(st.l, 16);
+  st.l += __shfl_xor(st.l, 32);
   if (g < G) {
     if (r == 0) {
-      sm_ml[w][0][g] = m_run;
-      sm_ml[w][1][g] = l_run;
+      sm.ml[w][0][g] = st.m;
+      sm.ml[w][1][g] = st.l;
     }
 #pragma unroll
     for (int mm = 0; mm < kMM; ++mm) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) sm_o[w][g][(D / 16) * (4 * r + rr) + mm] = acc[mm][rr];
+      for (int rr = 0; rr < 4; ++rr) sm.o[w][g][(D / 16) * (4 * r + rr) + mm] = st.acc[mm][rr];
     }
   }
   __syncthreads();
-
+  const int P = prm.max_partitions;
+  const int Hq = prm.num_q_heads;
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int gg = idx / D, d = idx % D;
     float M = kNegInf;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_ml[ww][0][gg]);
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.ml[ww][0][gg]);
     float lsum = 0.f, o = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      const float mw = sm_ml[ww][0][gg];
+      const float mw = sm.ml[ww][0][gg];
       const float f = mw == kNegInf ? 0.f : fast_exp2(mw - M);
-      lsum += f * sm_ml[ww][1][gg];
-      o += f * sm_o[ww][gg][d];
+      lsum += f * sm.ml[ww][1][gg];
+      o += f * sm.o[ww][gg][d];
     }
     const size_t row = (size_t)s * Hq + (size_t)h * G + gg;
-    if (nparts == 1) {
+    if (nparts <= 1) {
       store_out<DT>(prm.out, row * D + d, lsum > 0.f ? o / lsum : 0.f);
     } else {
       const size_t prow = row * P + p;
@@ -386,10 +396,317 @@ __global__ __launch_bounds__(kThreads) void attn_partition_kernel(AttnParams prm
       }
     }
   }
+  __syncthreads();
 }
 
-// Merge the partitions of one (sequence, query head): one wave, lanes over
+// One item's coordinates and extent, uniform across the workgroup.
+struct Item {
+  int s, h, p;
+  int ctx;     // context length of sequence s
+  int nparts;  // its partitions (0 for an empty context)
+  int tok0;    // first token of partition p
+  int nsub;    // 16-token sub-tiles holding tokens of this partition
+  int niter;   // ring steps per wave: max(1, ceil(nsub / 4))
+};
+
+__device__ __forceinline__ Item make_item(int s, int h, int p, int ctx) {
+  Item it;
+  it.s = s;
+  it.h = h;
+  it.p = p;
+  it.ctx = ctx;
+  it.nparts = (ctx + kPartitionTokens - 1) / kPartitionTokens;
+  it.tok0 = p * kPartitionTokens;
+  int ntok = ctx - it.tok0;
+  ntok = ntok < 0 ? 0 : (ntok > kPartitionTokens ? kPartitionTokens : ntok);
+  it.nsub = (ntok + kSub - 1) / kSub;
+  const int n = (it.nsub + kWaves - 1) / kWaves;
+  it.niter = n > 0 ? n : 1;
+  return it;
+}
+
+// Block ids of a wave's sub-tiles of an item: lane i holds the id for step i
+// (sub-tile w + 4i), -1 where that sub-tile holds no token.
+template <int BS>
+__device__ __forceinline__ int load_ids(const AttnParams& prm, const Item& it, int w, int lane) {
+  const int j = w + kWaves * lane;
+  int id = -1;
+  if (lane < it.niter && j < it.nsub)
+    id = prm.block_tables[(size_t)it.s * prm.max_blocks_per_seq + (it.tok0 + kSub * j) / BS];
+  return id;
+}
+
+template <int DT, int D, int BS>
+struct Geometry {
+  static constexpr int EB = Elem<DT>::bytes;
+  static constexpr int N = D * EB / 64;  // 16-byte K chunks per lane per sub-tile
+  static constexpr int kRow = D * EB;    // bytes per token row
+  static constexpr int kMM = D / 16;     // PV passes (MFMA row blocks of the head dim)
+  static constexpr int kTileBytes = BS * kRow;
+  static_assert(kPartitionTokens % BS == 0 && BS % kSub == 0, "partition/block sizes");
+};
+
+// Issue the loads of step i of item `it` for wave w.  A step whose sub-tile
+// holds no token, or whose block id lies outside the pool, gets a zero-length
+// resource: its loads return zeros and touch no memory.
+template <int DT, int D, int BS>
+__device__ __forceinline__ void issue_step(Tile<Geometry<DT, D, BS>::N>& t, const AttnParams& prm,
+                                           const Item& it, int ids, int i, int w, int koff, int voff) {
+  using Geo = Geometry<DT, D, BS>;
+  const int j = w + kWaves * i;
+  int phys = __builtin_amdgcn_readlane(ids, i);
+  const bool ok = j < it.nsub && (unsigned)phys < (unsigned)prm.num_blocks;
+  phys = ok ? phys : 0;
+  const size_t tile = ((size_t)phys * prm.num_kv_heads + it.h) * Geo::kTileBytes;
+  const int soff = ((it.tok0 + kSub * j) % BS) * Geo::kRow;
+  const int nrec = ok ? Geo::kTileBytes : 0;
+  load_tile<Geo::N>(t, make_rsrc(static_cast<const char*>(prm.k_cache) + tile, nrec),
+                    make_rsrc(static_cast<const char*>(prm.v_cache) + tile, nrec), koff, voff, soff);
+}
+
+// Tokens of step i of item `it` (for wave w) that are real: 0..16.
+__device__ __forceinline__ int step_valid(const AttnParams& prm, const Item& it, int ids, int i, int w) {
+  const int j = w + kWaves * i;
+  const int phys = __builtin_amdgcn_readlane(ids, i);
+  if (j >= it.nsub || (unsigned)phys >= (unsigned)prm.num_blocks) return 0;
+  const int v = it.ctx - (it.tok0 + kSub * j);
+  return v > kSub ? kSub : v;
+}
+
+// ---------------------------------------------------------------------------
+// Persistent kernel: dense work list, ring across items.
+// ---------------------------------------------------------------------------
+
+template <int DT, int D, int BS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_persistent_kernel(AttnParams prm) {
+  using Geo = Geometry<DT, D, BS>;
+  constexpr int N = Geo::N;
+  constexpr int kMM = Geo::kMM;
+  __shared__ MergeSmem<D> sm;
+  __shared__ int sm_pref[kMaxPersistentSeqs + 1];  // first item of each sequence
+  __shared__ int sm_ctx[kMaxPersistentSeqs];
+  __shared__ int sm_scan[kWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int r = lane >> 4;
+  const int B = prm.num_seqs;
+  const int G = prm.group;
+  const int Hq = prm.num_q_heads;
+
+  // ---- work list: items of sequence s are [pref[s], pref[s+1]) -------------
+  // An empty context still owns one item, which writes its zero row.
+  const int per = (B + kThreads - 1) / kThreads;
+  const int s_first = tid * per;
+  int mine = 0;
+  for (int k = 0; k < per; ++k) {
+    const int s = s_first + k;
+    if (s < B) {
+      int c = prm.context_lens[s];
+      c = c < 0 ? 0 : (c > prm.max_context_len ? prm.max_context_len : c);
+      sm_ctx[s] = c;
+      const int np = (c + kPartitionTokens - 1) / kPartitionTokens;
+      mine += np > 0 ? np : 1;
+    }
+  }
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) sm_scan[w] = incl;
+  __syncthreads();
+  int run = incl - mine;
+  for (int ww = 0; ww < w; ++ww) run += sm_scan[ww];
+  for (int k = 0; k < per; ++k) {
+    const int s = s_first + k;
+    if (s < B) {
+      sm_pref[s] = run;
+      const int np = (sm_ctx[s] + kPartitionTokens - 1) / kPartitionTokens;
+      run += np > 0 ? np : 1;
+    }
+  }
+  if (tid == 0) sm_pref[B] = sm_scan[0] + sm_scan[1] + sm_scan[2] + sm_scan[3];
+  __syncthreads();
+
+  const int T = uniform(sm_pref[B]);  // items per kv head
+  const long long n_items = (long long)prm.num_kv_heads * T;
+  const int xcd = blockIdx.x % kXcds;
+  const int nloc = gridDim.x / kXcds;  // workgroups per XCD (the grid is a multiple of 8)
+  const long long lo = n_items * xcd / kXcds;
+  const long long hi = n_items * (xcd + 1) / kXcds;
+  const long long first = lo + blockIdx.x / kXcds;
+  if (first >= hi) return;
+  const int nmine = (int)((hi - first + nloc - 1) / nloc);
+
+  // item number k of this workgroup -> coordinates (binary search in LDS)
+  auto item_at = [&](int k) -> Item {
+    const long long j = first + (long long)k * nloc;
+    const int h = (int)(j / T);
+    const int rr = (int)(j - (long long)h * T);
+    int a = 0, b = B - 1;
+    while (a < b) {
+      const int mid = (a + b + 1) >> 1;
+      if (uniform(sm_pref[mid]) <= rr) a = mid; else b = mid - 1;
+    }
+    return make_item(a, h, rr - uniform(sm_pref[a]), uniform(sm_ctx[a]));
+  };
+
+  const int koff = 16 * lane;
+  char* kst = reinterpret_cast<char*>(&sm.o[w][0][0]);  // this wave's K staging slot
+  const int voff = (4 * r) * Geo::kRow + (lane & 15) * (4 * N);
+  const float scale_log2 = prm.scale_log2;
+
+  // current item and the one after it (prefetched ids and query)
+  Item cur = item_at(0);
+  int ids_cur = load_ids<BS>(prm, cur, w, lane);
+  uint4 q_cur[N], q_nxt[N];
+  load_query<N>(q_cur, prm.q, cur.s, cur.h, G, Hq, lane);
+  int k_cur = 0;
+  const bool has_nxt0 = nmine > 1;
+  Item nxt = has_nxt0 ? item_at(1) : cur;
+  int ids_nxt = has_nxt0 ? load_ids<BS>(prm, nxt, w, lane) : -1;
+  if (has_nxt0) {
+    load_query<N>(q_nxt, prm.q, nxt.s, nxt.h, G, Hq, lane);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < N; ++kk) q_nxt[kk] = q_cur[kk];
+  }
+
+  WaveState<kMM> st;
+  st.reset();
+  int i_cur = 0;  // next step of the current item to compute
+
+  // issue cursor: item cur (+0) or nxt (+1) and step; beyond nxt = bubble
+  int iq_rel = 0, iq_step = 0;
+  auto issue_next = [&](Tile<N>& t) -> bool {
+    bool real = false;
+    if (iq_rel == 0) {
+      issue_step<DT, D, BS>(t, prm, cur, ids_cur, iq_step, w, koff, voff);
+      real = true;
+      if (++iq_step == cur.niter) { iq_rel = 1; iq_step = 0; }
+    } else if (iq_rel == 1 && k_cur + 1 < nmine) {
+      issue_step<DT, D, BS>(t, prm, nxt, ids_nxt, iq_step, w, koff, voff);
+      real = true;
+      if (++iq_step == nxt.niter) { iq_rel = 2; iq_step = 0; }
+    } else {
+      // keep the per-slot load count fixed: a zero-length resource reads nothing
+      load_tile<N>(t, make_rsrc(prm.k_cache, 0), make_rsrc(prm.v_cache, 0), koff, voff, 0);
+    }
+    return real;
+  };
+
+  // compute one slot; returns true when this workgroup's work is finished
+  auto step = [&](Tile<N>& t, bool real) -> bool {
+    if (!real) return false;
+    const int valid = step_valid(prm, cur, ids_cur, i_cur, w);
+    if (valid > 0) attend_subtile<DT, N, kMM>(t, q_cur, valid, scale_log2, r, st, kst);
+    if (++i_cur < cur.niter) return false;
+    merge_item<DT, D, kMM>(sm, st, prm, w, lane, cur.s, cur.h, cur.p, cur.nparts);
+    st.reset();
+    if (++k_cur >= nmine) return true;
+    cur = nxt;
+    ids_cur = ids_nxt;
+#pragma unroll
+    for (int kk = 0; kk < N; ++kk) q_cur[kk] = q_nxt[kk];
+    i_cur = 0;
+    iq_rel -= 1;
+    if (k_cur + 1 < nmine) {
+      nxt = item_at(k_cur + 1);
+      ids_nxt = load_ids<BS>(prm, nxt, w, lane);
+      load_query<N>(q_nxt, prm.q, nxt.s, nxt.h, G, Hq, lane);
+    }
+    return false;
+  };
+
+  Tile<N> t0, t1, t2;
+  bool r0 = issue_next(t0);
+  bool r1 = issue_next(t1);
+  bool r2;
+  for (;;) {
+    r2 = issue_next(t2);
+    if (step(t0, r0)) break;
+    r0 = issue_next(t0);
+    if (step(t1, r1)) break;
+    r1 = issue_next(t1);
+    if (step(t2, r2)) break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Grid kernel: one workgroup per possible item (any batch size).
+// ---------------------------------------------------------------------------
+
+template <int DT, int D, int BS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_grid_kernel(AttnParams prm) {
+  using Geo = Geometry<DT, D, BS>;
+  constexpr int N = Geo::N;
+  constexpr int kMM = Geo::kMM;
+  __shared__ MergeSmem<D> sm;
+
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const int r = lane >> 4;
+
+  // Logical order (kv head, partition, sequence): each XCD gets a range of
+  // kv heads, and inside it the first partitions of every sequence come
+  // before the later ones, so workgroups of short sequences' missing
+  // partitions (which exit at once) are dispatched last.
+  const int P = prm.max_partitions;
+  const int B = prm.num_seqs;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = L / (P * B);
+  const int p = (L / B) % P;
+  const int s = L % B;
+
+  int ctx = prm.context_lens[s];
+  ctx = ctx < 0 ? 0 : (ctx > prm.max_context_len ? prm.max_context_len : ctx);
+  const Item it = make_item(s, h, p, ctx);
+  if (p >= (it.nparts > 0 ? it.nparts : 1)) return;
+
+  const int ids = load_ids<BS>(prm, it, w, lane);
+  uint4 qb[N];
+  load_query<N>(qb, prm.q, s, h, prm.group, prm.num_q_heads, lane);
+  const int koff = 16 * lane;
+  char* kst = reinterpret_cast<char*>(&sm.o[w][0][0]);  // this wave's K staging slot
+  const int voff = (4 * r) * Geo::kRow + (lane & 15) * (4 * N);
+  const float scale_log2 = prm.scale_log2;
+
+  WaveState<kMM> st;
+  st.reset();
+  auto compute = [&](Tile<N>& t, int i) {
+    const int valid = step_valid(prm, it, ids, i, w);
+    if (valid > 0) attend_subtile<DT, N, kMM>(t, qb, valid, scale_log2, r, st, kst);
+  };
+  // 3-deep ring within the item; issue indices are clamped so every slot has
+  // the same load count.
+  const int last = it.niter - 1;
+  Tile<N> t0, t1, t2;
+  issue_step<DT, D, BS>(t0, prm, it, ids, 0, w, koff, voff);
+  issue_step<DT, D, BS>(t1, prm, it, ids, min(1, last), w, koff, voff);
+  int i = 0;
+  for (; i + 2 < it.niter; i += 3) {
+    issue_step<DT, D, BS>(t2, prm, it, ids, i + 2, w, koff, voff);
+    compute(t0, i);
+    issue_step<DT, D, BS>(t0, prm, it, ids, min(i + 3, last), w, koff, voff);
+    compute(t1, i + 1);
+    issue_step<DT, D, BS>(t1, prm, it, ids, min(i + 4, last), w, koff, voff);
+    compute(t2, i + 2);
+  }
+  if (i < it.niter) compute(t0, i);
+  if (i + 1 < it.niter) compute(t1, i + 1);
+  merge_item<DT, D, kMM>(sm, st, prm, w, lane, s, h, p, it.nparts);
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the partitions of one (sequence, query head): one wave, lanes over
 // the head dim, partitions visited in logical order.
+// ---------------------------------------------------------------------------
+
 template <int DT, int D>
 __global__ __launch_bounds__(64) void attn_reduce_kernel(AttnParams prm) {
   const int lane = threadIdx.x;
@@ -415,6 +732,7 @@ __global__ __launch_bounds__(64) void attn_reduce_kernel(AttnParams prm) {
 #pragma unroll
   for (int j = 0; j < kPer; ++j) o[j] = 0.f;
   float lsum = 0.f;
+#pragma unroll 4
   for (int p = 0; p < nparts; ++p) {
     const float mp = ml[2 * p];
     const float f = mp == kNegInf ? 0.f : fast_exp2(mp - M);
@@ -425,16 +743,21 @@ __global__ __launch_bounds__(64) void attn_reduce_kernel(AttnParams prm) {
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   const size_t orow = ((size_t)s * Hq + hq) * D;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) store_out<DT>(prm.out, orow + lane + 64 * j, lsum > 0.f ? o[j] * inv : 0.f);
+  for (int j = 0; j < kPer; ++j) store_out<DT>(prm.out, orow + lane + 64 * j, o[j] * inv);
 }
 
 template <int DT, int D, int BS>
-hipError_t launch_typed(const AttnParams& prm, hipStream_t stream) {
-  const long long nwg = (long long)prm.num_seqs * prm.num_kv_heads * prm.max_partitions;
-  if (nwg <= 0) return hipSuccess;
-  if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_partition_kernel<DT, D, BS>), dim3((unsigned)nwg), dim3(kThreads), 0,
-                     stream, prm);
+hipError_t launch_typed(const AttnParams& prm, int persistent_wgs, hipStream_t stream) {
+  const dim3 block(kThreads);
+  if (persistent_wgs > 0 && prm.num_seqs <= kMaxPersistentSeqs) {
+    hipLaunchKernelGGL((attn_persistent_kernel<DT, D, BS>), dim3((unsigned)persistent_wgs), block,
+                       0, stream, prm);
+  } else {
+    const long long nwg = (long long)prm.num_seqs * prm.num_kv_heads * prm.max_partitions;
+    if (nwg <= 0) return hipSuccess;
+    if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((attn_grid_kernel<DT, D, BS>), dim3((unsigned)nwg), block, 0, stream, prm);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || prm.max_partitions <= 1) return err;
   hipLaunchKernelGGL((attn_reduce_kernel<DT, D>), dim3((unsigned)(prm.num_seqs * prm.num_q_heads)),
@@ -443,19 +766,19 @@ hipError_t launch_typed(const AttnParams& prm, hipStream_t stream) {
 }
 
 template <int DT, int D>
-hipError_t launch_bs(const AttnParams& prm, int bs, hipStream_t stream) {
+hipError_t launch_bs(const AttnParams& prm, int bs, int persistent_wgs, hipStream_t stream) {
   switch (bs) {
-    case 16: return launch_typed<DT, D, 16>(prm, stream);
-    case 32: return launch_typed<DT, D, 32>(prm, stream);
+    case 16: return launch_typed<DT, D, 16>(prm, persistent_wgs, stream);
+    case 32: return launch_typed<DT, D, 32>(prm, persistent_wgs, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int DT>
-hipError_t launch_d(const AttnParams& prm, int d, int bs, hipStream_t stream) {
+hipError_t launch_d(const AttnParams& prm, int d, int bs, int persistent_wgs, hipStream_t stream) {
   switch (d) {
-    case 64: return launch_bs<DT, 64>(prm, bs, stream);
-    case 128: return launch_bs<DT, 128>(prm, bs, stream);
+    case 64: return launch_bs<DT, 64>(prm, bs, persistent_wgs, stream);
+    case 128: return launch_bs<DT, 128>(prm, bs, persistent_wgs, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -463,11 +786,11 @@ hipError_t launch_d(const AttnParams& prm, int d, int bs, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_paged_attention(const AttnParams& prm, int dtype, int head_dim,
-                                  int block_size, hipStream_t stream) {
+                                  int block_size, int persistent_wgs, hipStream_t stream) {
   switch (dtype) {
-    case DT_F32: return launch_d<DT_F32>(prm, head_dim, block_size, stream);
-    case DT_F16: return launch_d<DT_F16>(prm, head_dim, block_size, stream);
-    case DT_BF16: return launch_d<DT_BF16>(prm, head_dim, block_size, stream);
+    case DT_F32: return launch_d<DT_F32>(prm, head_dim, block_size, persistent_wgs, stream);
+    case DT_F16: return launch_d<DT_F16>(prm, head_dim, block_size, persistent_wgs, stream);
+    case DT_BF16: return launch_d<DT_BF16>(prm, head_dim, block_size, persistent_wgs, stream);
     default: return hipErrorInvalidValue;
   }
 }

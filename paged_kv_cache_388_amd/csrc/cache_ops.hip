@@ -66,6 +66,36 @@ __global__ __launch_bounds__(kThreads) void stream_copy_kernel(uint4* __restrict
     dst[c] = src[c];
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Read-only stream: workgroup b reads the contiguous range
+// [b * per_wg, (b + 1) * per_wg) of 16-byte chunks with nontemporal loads,
+// eight in flight per thread, folds them with XOR and writes one word, so the
+// loads cannot be dropped.
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __restrict__ src,
+                                                               int64_t chunks, int64_t per_wg,
+                                                               uint32_t* __restrict__ sink) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t begin = (int64_t)blockIdx.x * per_wg;
+  const int64_t end = begin + per_wg < chunks ? begin + per_wg : chunks;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  int64_t c = begin + threadIdx.x;
+  for (; c + 7 * kThreads < end; c += 8 * kThreads) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + c + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u];
+  }
+  for (; c < end; c += kThreads) acc ^= __builtin_nontemporal_load(src + c);
+  uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x ^= __shfl_xor(x, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
 }  // namespace
 
 hipError_t launch_kv_append(const void* key, const void* value, void* k_cache, void* v_cache,
@@ -102,6 +132,19 @@ hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStrea
   if (nwg > 256 * 64) nwg = 256 * 64;  // grid-stride beyond 64 workgroups per CU
   hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)nwg), dim3(kThreads), 0, stream,
                      static_cast<uint4*>(dst), static_cast<const uint4*>(src), chunks);
+  return hipGetLastError();
+}
+
+}  // namespace pkv
+
+namespace pkv {
+
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  const int64_t chunks = (int64_t)(bytes / 16);
+  if (chunks == 0) return hipSuccess;
+  const int64_t per_wg = (chunks + kStreamReadWorkgroups - 1) / kStreamReadWorkgroups;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(kStreamReadWorkgroups), dim3(kThreads), 0, stream,
+                     static_cast<const u32x4*>(src), chunks, per_wg, sink);
   return hipGetLastError();
 }
 

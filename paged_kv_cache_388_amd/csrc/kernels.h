@@ -33,10 +33,16 @@ struct AttnParams {
   float scale_log2;             // scale * log2(e): logits kept in base-2 units
 };
 
-// dtype: 0 f32, 1 f16, 2 bf16.  Returns hipErrorInvalidValue for a
-// (dtype, head_dim, block_size) combination that is not instantiated.
+// Largest batch the persistent attention kernel takes (its work list lives in
+// LDS); larger batches use the grid kernel.
+constexpr int kMaxPersistentSeqs = 2048;
+
+// dtype: 0 f32, 1 f16, 2 bf16.  persistent_wgs: workgroups of the persistent
+// kernel (a multiple of 8), or 0 for the grid kernel.  Returns
+// hipErrorInvalidValue for a (dtype, head_dim, block_size) combination that
+// is not instantiated.
 hipError_t launch_paged_attention(const AttnParams& p, int dtype, int head_dim,
-                                  int block_size, hipStream_t stream);
+                                  int block_size, int persistent_wgs, hipStream_t stream);
 
 hipError_t launch_kv_append(const void* key, const void* value, void* k_cache,
                             void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
@@ -48,5 +54,9 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block
                               hipStream_t stream);
 
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+// sink: kStreamReadWorkgroups uint32 words, one per workgroup.
+constexpr int kStreamReadWorkgroups = 256 * 8;
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 }  // namespace pkv

@@ -5,6 +5,9 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+
+#include <atomic>
 
 #include <hip/hip_runtime_api.h>
 
@@ -51,6 +54,31 @@ pkv_status check_pool(const pkv_pool& pool) {
 
 size_t pool_block_bytes(const pkv_pool& pool) {
   return (size_t)pool.num_kv_heads * pool.block_size * pool.head_dim * elem_bytes(pool.dtype);
+}
+
+// Workgroups of the persistent attention kernel on the current device: two
+// per compute unit (its occupancy), rounded down to a multiple of the 8 XCDs.
+// The grid kernel is the default; PAGEDKV_PERSISTENT=1 selects the persistent
+// one (read once per process).
+int persistent_workgroups() {
+  static const bool enabled = [] {
+    const char* e = getenv("PAGEDKV_PERSISTENT");
+    return e && atoi(e) == 1;
+  }();
+  if (!enabled) return 0;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int wgs = cached[dev].load(std::memory_order_relaxed);
+  if (wgs == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    wgs = (2 * cus) / 8 * 8;
+    if (wgs <= 0) wgs = -1;
+    cached[dev].store(wgs, std::memory_order_relaxed);
+  }
+  return wgs > 0 ? wgs : 0;
 }
 
 int32_t partitions_for(int32_t max_context_len) {
@@ -156,7 +184,8 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_cache,
   const size_t po = (size_t)num_seqs * num_q_heads * prm.max_partitions * pool.head_dim;
   prm.part_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
   prm.part_ml = need > 0 ? static_cast<float*>(workspace) + po : nullptr;
-  hipError_t err = pkv::launch_paged_attention(prm, pool.dtype, pool.head_dim, pool.block_size, stream);
+  hipError_t err = pkv::launch_paged_attention(prm, pool.dtype, pool.head_dim, pool.block_size,
+                                               persistent_workgroups(), stream);
   return err == hipSuccess ? PKV_OK : hip_fail(err, "paged_attention_decode launch");
 }
 
@@ -183,6 +212,16 @@ pkv_status pkv_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t
     return fail(PKV_EINVAL, "pointers and byte count must be multiples of 16");
   hipError_t err = pkv::launch_stream_copy(dst, src, bytes, stream);
   return err == hipSuccess ? PKV_OK : hip_fail(err, "pkv_stream_copy launch");
+}
+
+pkv_status pkv_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (bytes == 0) return PKV_OK;
+  if (!src || !sink) return fail(PKV_EINVAL, "null pointer argument");
+  if (!aligned16(src) || (bytes & 15u))
+    return fail(PKV_EINVAL, "src and byte count must be multiples of 16");
+  hipError_t err = pkv::launch_stream_read(src, bytes, sink, stream);
+  return err == hipSuccess ? PKV_OK : hip_fail(err, "pkv_stream_read launch");
 }
 
 }  // extern "C"

@@ -176,3 +176,17 @@ def test_caller_stream_is_used():
         out = dw.attend()
     s.synchronize()
     check_attention(to_host(out, "f16"), oracle_step(w), "f16", "side stream")
+
+
+def test_large_batch_uses_grid_kernel_path():
+    # more sequences than the persistent kernel's LDS work list holds
+    rng = np.random.default_rng(12)
+    ctx = rng.integers(0, 700, size=2100)
+    w = wl.build("bigbatch", 12, rng, ctx, 4, 2, 64, 16, "bf16")
+    _run_and_check(w, "B=2100")
+
+
+def test_single_sequence_many_partitions():
+    rng = np.random.default_rng(13)
+    w = wl.build("long1", 13, rng, [20000], 8, 1, 128, 32, "bf16", poison=True)
+    _run_and_check(w, "one long sequence")
