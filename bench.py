@@ -10,10 +10,13 @@ resident in HBM before timing starts.
 
 Prints ONE JSON line.  ``value`` is the KV bytes a step reads (each cached
 token's K and V once) divided by the measured step time, in GB/s.
-``roofline`` prices the attention kernels (partition + merge, launched by one
-paged_attention_decode call) against MI355X's 8 TB/s HBM peak, with their
-duration measured by HIP events on the launching stream.  ``cpu_baseline``
-times the CPU oracle on the same step's inputs.
+``roofline`` prices the decode call (the stream kernel and its piece merge,
+launched by one paged_attention_decode call) against MI355X's 8 TB/s HBM
+peak, with its duration measured by HIP events on the launching stream;
+``traffic`` is the HBM bytes the rocprofv3 counters measured for that call
+(profiles/, calibrated against a plain copy), reported only while the kernel
+source is the one the counters were taken on.  ``cpu_baseline`` times the CPU
+oracle on the same step's inputs.
 """
 
 import argparse
@@ -30,6 +33,8 @@ sys.path.insert(0, ROOT)
 from paged_kv_cache_388_amd import workloads as wl  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
+ATTN_SOURCE = os.path.join(ROOT, "paged_kv_cache_388_amd", "csrc", "attention.hip")
+PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) and seqs/s"
 
 
@@ -42,14 +47,36 @@ def algorithmic_bytes(w):
             + 4 * w.num_seqs)
 
 
-def cpu_baseline(w, max_seconds):
+def counter_traffic(workload):
+    """HBM bytes per decode call from the committed counter summary of this
+    workload, or None if there is none or the kernel source has changed since
+    the counters were taken (the summary records the source's SHA-256)."""
+    import hashlib
+    path = os.path.join(PROFILES, f"attn_stream_kernel_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.strip().startswith(("traffic_bytes_per_call", "source_sha256")):
+                k, v = line.strip().split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    with open(ATTN_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("source_sha256") != sha or "traffic_bytes_per_call" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_call"])
+
+
+def cpu_baseline(w, min_seconds):
     """The fp64 oracle on this step's inputs, single-threaded (BLAS pinned to
-    one thread): append into the host pools, then attention over as many
-    sequences as fit in about ``max_seconds``.  Rate in KV GB/s of the
-    sequences it finished."""
+    one thread): the step's cache writes into the host pools, then attention
+    over every sequence, repeated until about ``min_seconds`` have passed.
+    Rate in KV GB/s (and sequences/s) of the attention passes it finished."""
     from threadpoolctl import threadpool_limits
 
     import oracle
+    b = wl.ELEM_BYTES[w.dtype]
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         kc, vc = w.k_cache, w.v_cache
@@ -57,20 +84,25 @@ def cpu_baseline(w, max_seconds):
             kc, vc = oracle.copy_blocks(kc, vc, w.block_mapping)
         if len(w.slot_mapping):
             kc, vc = oracle.kv_append(kc, vc, w.new_key, w.new_value, w.slot_mapping)
-        done = []
-        for s in range(w.num_seqs):
-            oracle.decode_attention(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
-                                    w.dtype, seq_ids=[s])
-            done.append(s)
-            if time.perf_counter() - t0 > max_seconds:
+        t1 = time.perf_counter()
+        seqs = 0
+        kv = 0
+        while True:
+            for s in range(w.num_seqs):
+                oracle.decode_attention(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                                        w.dtype, seq_ids=[s])
+                seqs += 1
+                kv += 2 * int(w.context_lens[s]) * w.num_kv_heads * w.head_dim * b
+                if time.perf_counter() - t1 > min_seconds:
+                    break
+            if time.perf_counter() - t1 > min_seconds:
                 break
-        dt = time.perf_counter() - t0
-    b = wl.ELEM_BYTES[w.dtype]
-    kv = 2 * int(w.context_lens[done].astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * b
-    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{len(done)} of {w.num_seqs} sequences of the same step "
-                       f"(append + attention), fp64 NumPy, {dt:.1f} s"),
-            "seqs_per_s": len(done) / dt}
+        dt = time.perf_counter() - t1
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{seqs} sequence-attentions of this step ({seqs / w.num_seqs:.2f} passes "
+                       f"over the {w.num_seqs}-sequence batch) after its cache writes "
+                       f"({t1 - t0:.1f} s), fp64 NumPy, one thread, {dt:.1f} s"),
+            "seqs_per_s": round(seqs / dt, 2)}
 
 
 def copy_probe(mib, steps, warmup):
@@ -135,8 +167,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b_gqa",
                     help="one of: " + ", ".join(wl.NAMED[:4]) + ", long_ctx_bs16, long_ctx_bs32")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="bound on the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="duration of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--read-probe-mib", type=int, default=0,
                     help="instead of the decode step, time pkv_stream_read of this many MiB "
                          "(the achievable read-bandwidth reference)")
@@ -146,7 +178,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
@@ -187,9 +219,9 @@ def main():
     slot_mapping = up(w.slot_mapping.astype(np.int32))
     new_key, new_value = up(w.new_key), up(w.new_value)
     out = torch.empty_like(q)
-    ws_bytes = _lib.paged_attention_workspace_bytes(w.num_seqs, w.num_q_heads, w.head_dim,
+    ws_bytes = _lib.paged_attention_workspace_bytes(k_cache, w.num_seqs, w.num_q_heads,
                                                     w.max_context_len)
-    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    workspace = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     max_ctx = w.max_context_len
     torch.cuda.synchronize()
 
@@ -256,8 +288,9 @@ def main():
                          "p90": round(float(np.percentile(attn_ms, 90)), 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None,
-                     "kernel": "attn_partition_kernel + attn_reduce_kernel (one decode call)",
+                     "traffic": counter_traffic(w.name),
+                     "kernel": (f"attn_stream_kernel<{w.dtype},{w.head_dim},{w.block_size}> + "
+                                "attn_stream_merge_kernel (one paged_attention_decode call)"),
                      "algorithmic_bytes_per_launch": alg},
         "cpu_baseline": cpu,
     }

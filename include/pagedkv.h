@@ -27,8 +27,8 @@
  *    then holds a message (per calling thread).
  *  - Device-side metadata (block ids, context lengths, slots) is trusted for
  *    correctness but never for memory safety: a block id or slot outside the
- *    pool is skipped instead of dereferenced, and a context length is clamped
- *    to [0, max_context_len].
+ *    pool is never dereferenced, and a context length is clamped to
+ *    [0, max_context_len].
  *  - Thread safety: the library keeps no mutable global state apart from the
  *    per-thread error message.  Calls on different streams may overlap.
  */
@@ -66,7 +66,8 @@ typedef struct {
   int32_t dtype;         /* pkv_dtype */
 } pkv_pool;
 
-/* Tokens per split-context partition of paged_attention_decode (512). */
+/* Tokens per split-context partition of paged_attention_decode for batches
+ * above 4096 sequences (512); smaller batches split at 16-token granularity. */
 PKV_API int32_t pkv_partition_tokens(void);
 
 /*
@@ -89,12 +90,16 @@ PKV_API pkv_status paged_kv_append(const void* key, const void* value,
                                    hipStream_t stream);
 
 /*
- * Bytes of workspace paged_attention_decode needs for this shape: fp32
- * partial states of every (sequence, query head, partition) when a context
- * can span more than one partition, else 0.  Returns 0 for invalid input.
+ * Bytes of workspace paged_attention_decode needs for this shape on the
+ * current device (the kernel's grid follows the device's compute-unit count):
+ * per-sequence sub-tile offsets and fp32 partial softmax states of the
+ * sequences whose context is split between waves.  Independent of the context
+ * lengths for batches up to 4096 sequences; above that it grows with
+ * ceil(max_context_len / 512).  Returns 0 for invalid input (including
+ * num_q_heads not a multiple of pool.num_kv_heads).
  */
-PKV_API size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
-                                               int32_t head_dim, int32_t max_context_len);
+PKV_API size_t paged_attention_workspace_bytes(pkv_pool pool, int32_t num_seqs,
+                                               int32_t num_q_heads, int32_t max_context_len);
 
 /*
  * paged_attention_decode — one query token per sequence attends to its whole
@@ -109,10 +114,14 @@ PKV_API size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_h
  * over logical tokens t < n; token t lives in physical block
  * block_tables[s, t / block_size] at offset t % block_size.  n = 0 gives a
  * zero row.  Softmax and accumulation are fp32; out is rounded to nearest
- * even in the pool dtype.  Contexts longer than one partition are split into
- * partitions computed independently and merged exactly (log-sum-exp rescale);
- * the order of every reduction depends only on logical positions, so the
- * result is bit-identical under any physical placement of the blocks.
+ * even in the pool dtype.  The context is cut into 16-token sub-tiles; each
+ * wave of the kernel walks an equal run of them, and where a sequence's
+ * context is split between waves their partial states (running max,
+ * normaliser, unnormalised output) are merged exactly by a log-sum-exp
+ * rescale.  The split points depend only on the context lengths, and every
+ * reduction runs in logical token order, so the result is bit-identical under
+ * any physical placement of the blocks and across repeated calls.  A block id
+ * outside the pool is never dereferenced (its tokens read as zeros).
  *
  *   out           [num_seqs, num_q_heads, head_dim]  pool dtype, written
  *   q             [num_seqs, num_q_heads, head_dim]  pool dtype
@@ -124,8 +133,11 @@ PKV_API size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_h
  *   scale         logit scale, usually 1/sqrt(head_dim)
  *   max_context_len  host-known upper bound of context_lens (no device read);
  *                 max_blocks_per_seq * block_size must be >= it
- *   workspace     device buffer of >= paged_attention_workspace_bytes(...)
- *                 bytes (may be NULL when that is 0); contents are scratch
+ *   workspace     device buffer of >= paged_attention_workspace_bytes(pool,
+ *                 num_seqs, num_q_heads, max_context_len) bytes, 16-byte
+ *                 aligned (may be NULL when that is 0); contents are scratch,
+ *                 need no initialisation and must not be shared by calls
+ *                 that can run concurrently
  */
 PKV_API pkv_status paged_attention_decode(void* out, const void* q,
                                           const void* k_cache, const void* v_cache,

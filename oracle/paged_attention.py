@@ -25,7 +25,7 @@ What is computed, and where the pages state it
   block stays unchanged ("05 PagedAttention", section "KV Cache Sharing
   (Copy-on-Write)"; first page, section "Copy-on-Write"): ``copy_blocks``.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
 * pool layout ``[num_blocks, H_kv, block_size, D]`` for K and V alike;
 * query head h reads KV head ``h // G`` with ``G = H_q // H_kv``;
 * the single query attends to all ``context_lens[s]`` cached tokens, the token

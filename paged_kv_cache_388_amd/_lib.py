@@ -48,7 +48,7 @@ def load():
     lib.pkv_partition_tokens.restype = c_i32
     lib.paged_kv_append.argtypes = [c_vp, c_vp, c_vp, c_vp, PkvPool, c_vp, c_i32, c_vp]
     lib.paged_kv_append.restype = c_i32
-    lib.paged_attention_workspace_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32]
+    lib.paged_attention_workspace_bytes.argtypes = [PkvPool, c_i32, c_i32, c_i32]
     lib.paged_attention_workspace_bytes.restype = c_sz
     lib.paged_attention_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, PkvPool, c_vp, c_i32, c_vp,
                                            c_i32, c_i32, c_f, c_i32, c_vp, c_sz, c_vp]
@@ -132,9 +132,11 @@ def paged_kv_append(key, value, k_cache, v_cache, slot_mapping, stream=None):
                                   _ptr(slot_mapping), T, _stream(stream)))
 
 
-def paged_attention_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len):
-    return int(load().paged_attention_workspace_bytes(num_seqs, num_q_heads, head_dim,
-                                                      max_context_len))
+def paged_attention_workspace_bytes(k_cache, num_seqs, num_q_heads, max_context_len):
+    """Workspace bytes paged_attention_decode needs for this pool and batch
+    on the current device."""
+    return int(load().paged_attention_workspace_bytes(pool_of(k_cache), int(num_seqs),
+                                                      int(num_q_heads), int(max_context_len)))
 
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
@@ -142,7 +144,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over each sequence's
     paged context.  max_context_len is a host-side upper bound of
     context_lens.  workspace: a uint8 device tensor of at least
-    paged_attention_workspace_bytes(...) bytes, or None to allocate one."""
+    paged_attention_workspace_bytes(k_cache, ...) bytes, or None to allocate one."""
     pool = _pools(k_cache, v_cache)
     dev = k_cache.device
     _need(q, "q", dtype=k_cache.dtype, dim=3, device=dev)
@@ -154,9 +156,9 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     B, Hq, D = q.shape
     if block_tables.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("block_tables / context_lens disagree with q on num_seqs")
-    need = paged_attention_workspace_bytes(B, Hq, D, int(max_context_len))
+    need = paged_attention_workspace_bytes(k_cache, B, Hq, int(max_context_len))
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
     else:
         _need(workspace, "workspace", device=dev)
     _check(load().paged_attention_decode(

@@ -4,20 +4,17 @@
 // single new query over the sequence's cached context, gathered through its
 // block table (first page, "PagedAttention: Decoupling Logical Context from
 // Contiguous GPU Memory"; "The Memory Wall", "Show Me The Code: A Conceptual
-// PagedAttention Kernel", whose per-request loop over logical blocks with a
-// table lookup per block is the structure kept here).  Query head h reads KV
-// head h / G.
+// PagedAttention Kernel", whose loop over logical blocks with one table lookup
+// per block is the structure kept here).  Query head h reads KV head h / G.
 //
-// Work unit.  One item = (kv head, sequence, 512-token partition), handled by
-// one workgroup of 4 waves; all G query heads of the kv head share the K/V
-// bytes it streams, so every K/V byte crosses HBM once per step.  Wave w takes
-// the item's 16-token sub-tiles w, w+4, w+8, ...
-//
-// Per 16-token sub-tile a wave does:
+// The unit of work is a 16-token sub-tile of one (kv head, sequence): all G
+// query heads of the kv head share the K/V bytes it streams, so every K/V byte
+// crosses HBM once per call.  Per sub-tile a wave does:
 //   QK   S^T[16 tok x 16 cols] = K_tile[16 x D] . Q^T[D x 16] on MFMA
 //        (16x16x32 for fp16/bf16, 16x16x4 for fp32).  Column g < G is query
-//        head h*G+g; the other columns are zero padding.  Each lane's K load
-//        is a 16-byte piece of one token row, which is exactly its A operand.
+//        head h*G+g; the other columns are zero padding.  K is loaded as whole
+//        128-byte lines and re-dealt into the MFMA operand layout through the
+//        wave's LDS slot.
 //   mask tokens at or past the context length get -inf (a select, so stale
 //        or NaN bits in unused slots never reach the result).
 //   softmax  running max per column (3 ops in-lane + 2 cross-row shuffles),
@@ -30,20 +27,27 @@
 //        four token chunks the four k-values of its A operand (one v_perm_b32
 //        per pair).  P is split into hi + lo 16-bit parts so the product keeps
 //        ~16 mantissa bits instead of 8.
-// The reduction order depends only on logical token positions, never on
-// physical block ids or on which workgroup ran an item.
 //
-// Scheduling.  The persistent kernel launches two workgroups per CU.  Each
-// builds the dense list of non-empty items (prefix sum of partitions per
-// sequence, in LDS), takes a strided share of its XCD's contiguous range of
-// that list, and streams sub-tiles through a 3-deep register ring that runs
-// across item boundaries, with the next item's block ids and query prefetched
-// one item ahead.  The grid kernel (one workgroup per possible item) serves
-// batches too large for the LDS work list.
+// Stream path (batches up to kMaxStreamSeqs).  The work of a call is the
+// ordered list of positions (kv head, sequence, sub-tile).  Two workgroups per
+// CU stay resident for the whole call; each of their waves owns one equal,
+// contiguous chunk of that list and streams it through a 3-deep register ring
+// that runs across sequence boundaries, so every wave has the same number of
+// tiles and no slot idles between items.  The blockIdx -> chunk map is
+// XCD-aware: each XCD takes one contiguous range of the list (one kv head at
+// H_kv = 8), so sequences sharing blocks meet in the same L2.  A wave writes a
+// sequence it covers whole straight to `out`; a piece of a longer sequence
+// goes to one of the wave's two partial slots (its first and last piece), and
+// a second kernel merges the pieces of each split sequence in logical order.
 //
-// Partitions: a context longer than 512 tokens is split into 512-token
-// partitions whose (max, normaliser, unnormalised output) are merged by a
-// second kernel.  A single-partition context is finished in place.
+// Grid path (larger batches).  One workgroup of 4 waves per (kv head,
+// sequence, 512-token partition); wave w takes sub-tiles w, w+4, ...; the
+// waves merge in LDS and a second kernel merges the partitions.
+//
+// In both, every reduction order depends only on logical token positions and
+// context lengths, never on physical block ids or on which workgroup ran
+// what, so the result is bit-identical under any physical placement.
+
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -62,9 +66,9 @@ typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));  // cvt_pkrtz result
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = kStreamWaves;  // waves per workgroup, both paths
 constexpr int kThreads = 64 * kWaves;
-constexpr int kSub = 16;  // tokens per MFMA row group
+constexpr int kSub = kSubTokens;      // tokens per MFMA row group
 constexpr int kXcds = 8;
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -337,6 +341,60 @@ __device__ __forceinline__ void attend_subtile(Tile<N>& t, const uint4 (&qb)[N],
   }
 }
 
+template <int DT, int D, int BS>
+struct Geometry {
+  static constexpr int EB = Elem<DT>::bytes;
+  static constexpr int N = D * EB / 64;  // 16-byte K chunks per lane per sub-tile
+  static constexpr int kRow = D * EB;    // bytes per token row
+  static constexpr int kMM = D / 16;     // PV passes (MFMA row blocks of the head dim)
+  static constexpr int kTileBytes = BS * kRow;
+  static_assert(kPartitionTokens % BS == 0 && BS % kSub == 0, "partition/block sizes");
+};
+
+// Lane (r, g) of a finished wave state holds column g's accumulator rows
+// d = (D/16)*(4r + rr) + mm, i.e. the contiguous run d in [r*D/4, (r+1)*D/4)
+// in the order idx = rr*(D/16) + mm.  Gather that run.
+template <int D, int kMM>
+__device__ __forceinline__ void lane_run(float (&o)[D / 4], const WaveState<kMM>& st) {
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+    for (int mm = 0; mm < kMM; ++mm) o[rr * kMM + mm] = st.acc[mm][rr];
+}
+
+// Store a lane's run of D/4 values (already scaled) to `dst` (16-byte aligned)
+// in the pool dtype, as 16-byte vector stores.
+template <int DT, int D>
+__device__ __forceinline__ void store_run(void* dst, const float (&o)[D / 4]) {
+  if constexpr (DT == DT_F32) {
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i)
+      reinterpret_cast<float4*>(dst)[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+  } else {
+    uint32_t packed[D / 8];
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) {
+      uint16_t lo, hi;
+      if constexpr (DT == DT_F16) {
+        lo = __builtin_bit_cast(uint16_t, (_Float16)o[2 * i]);
+        hi = __builtin_bit_cast(uint16_t, (_Float16)o[2 * i + 1]);
+      } else {
+        lo = f32_to_bf16_rne(o[2 * i]);
+        hi = f32_to_bf16_rne(o[2 * i + 1]);
+      }
+      packed[i] = (uint32_t)lo | ((uint32_t)hi << 16);
+    }
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+      reinterpret_cast<uint4*>(dst)[i] =
+          make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
+  }
+}
+
+// ===========================================================================
+// Grid path
+// ===========================================================================
+
 // LDS used to merge the four waves' states of one item.  Between merges,
 // o[w] is wave w's private K staging slot (at least one 16-token sub-tile of
 // K: 16 * D * 4 bytes <= sizeof(o[w])).
@@ -436,15 +494,6 @@ __device__ __forceinline__ int load_ids(const AttnParams& prm, const Item& it, i
   return id;
 }
 
-template <int DT, int D, int BS>
-struct Geometry {
-  static constexpr int EB = Elem<DT>::bytes;
-  static constexpr int N = D * EB / 64;  // 16-byte K chunks per lane per sub-tile
-  static constexpr int kRow = D * EB;    // bytes per token row
-  static constexpr int kMM = D / 16;     // PV passes (MFMA row blocks of the head dim)
-  static constexpr int kTileBytes = BS * kRow;
-  static_assert(kPartitionTokens % BS == 0 && BS % kSub == 0, "partition/block sizes");
-};
 
 // Issue the loads of step i of item `it` for wave w.  A step whose sub-tile
 // holds no token, or whose block id lies outside the pool, gets a zero-length
@@ -474,170 +523,7 @@ __device__ __forceinline__ int step_valid(const AttnParams& prm, const Item& it,
 }
 
 // ---------------------------------------------------------------------------
-// Persistent kernel: dense work list, ring across items.
-// ---------------------------------------------------------------------------
-
-template <int DT, int D, int BS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_persistent_kernel(AttnParams prm) {
-  using Geo = Geometry<DT, D, BS>;
-  constexpr int N = Geo::N;
-  constexpr int kMM = Geo::kMM;
-  __shared__ MergeSmem<D> sm;
-  __shared__ int sm_pref[kMaxPersistentSeqs + 1];  // first item of each sequence
-  __shared__ int sm_ctx[kMaxPersistentSeqs];
-  __shared__ int sm_scan[kWaves];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = uniform(tid >> 6);
-  const int r = lane >> 4;
-  const int B = prm.num_seqs;
-  const int G = prm.group;
-  const int Hq = prm.num_q_heads;
-
-  // ---- work list: items of sequence s are [pref[s], pref[s+1]) -------------
-  // An empty context still owns one item, which writes its zero row.
-  const int per = (B + kThreads - 1) / kThreads;
-  const int s_first = tid * per;
-  int mine = 0;
-  for (int k = 0; k < per; ++k) {
-    const int s = s_first + k;
-    if (s < B) {
-      int c = prm.context_lens[s];
-      c = c < 0 ? 0 : (c > prm.max_context_len ? prm.max_context_len : c);
-      sm_ctx[s] = c;
-      const int np = (c + kPartitionTokens - 1) / kPartitionTokens;
-      mine += np > 0 ? np : 1;
-    }
-  }
-  int incl = mine;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) sm_scan[w] = incl;
-  __syncthreads();
-  int run = incl - mine;
-  for (int ww = 0; ww < w; ++ww) run += sm_scan[ww];
-  for (int k = 0; k < per; ++k) {
-    const int s = s_first + k;
-    if (s < B) {
-      sm_pref[s] = run;
-      const int np = (sm_ctx[s] + kPartitionTokens - 1) / kPartitionTokens;
-      run += np > 0 ? np : 1;
-    }
-  }
-  if (tid == 0) sm_pref[B] = sm_scan[0] + sm_scan[1] + sm_scan[2] + sm_scan[3];
-  __syncthreads();
-
-  const int T = uniform(sm_pref[B]);  // items per kv head
-  const long long n_items = (long long)prm.num_kv_heads * T;
-  const int xcd = blockIdx.x % kXcds;
-  const int nloc = gridDim.x / kXcds;  // workgroups per XCD (the grid is a multiple of 8)
-  const long long lo = n_items * xcd / kXcds;
-  const long long hi = n_items * (xcd + 1) / kXcds;
-  const long long first = lo + blockIdx.x / kXcds;
-  if (first >= hi) return;
-  const int nmine = (int)((hi - first + nloc - 1) / nloc);
-
-  // item number k of this workgroup -> coordinates (binary search in LDS)
-  auto item_at = [&](int k) -> Item {
-    const long long j = first + (long long)k * nloc;
-    const int h = (int)(j / T);
-    const int rr = (int)(j - (long long)h * T);
-    int a = 0, b = B - 1;
-    while (a < b) {
-      const int mid = (a + b + 1) >> 1;
-      if (uniform(sm_pref[mid]) <= rr) a = mid; else b = mid - 1;
-    }
-    return make_item(a, h, rr - uniform(sm_pref[a]), uniform(sm_ctx[a]));
-  };
-
-  const int koff = 16 * lane;
-  char* kst = reinterpret_cast<char*>(&sm.o[w][0][0]);  // this wave's K staging slot
-  const int voff = (4 * r) * Geo::kRow + (lane & 15) * (4 * N);
-  const float scale_log2 = prm.scale_log2;
-
-  // current item and the one after it (prefetched ids and query)
-  Item cur = item_at(0);
-  int ids_cur = load_ids<BS>(prm, cur, w, lane);
-  uint4 q_cur[N], q_nxt[N];
-  load_query<N>(q_cur, prm.q, cur.s, cur.h, G, Hq, lane);
-  int k_cur = 0;
-  const bool has_nxt0 = nmine > 1;
-  Item nxt = has_nxt0 ? item_at(1) : cur;
-  int ids_nxt = has_nxt0 ? load_ids<BS>(prm, nxt, w, lane) : -1;
-  if (has_nxt0) {
-    load_query<N>(q_nxt, prm.q, nxt.s, nxt.h, G, Hq, lane);
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < N; ++kk) q_nxt[kk] = q_cur[kk];
-  }
-
-  WaveState<kMM> st;
-  st.reset();
-  int i_cur = 0;  // next step of the current item to compute
-
-  // issue cursor: item cur (+0) or nxt (+1) and step; beyond nxt = bubble
-  int iq_rel = 0, iq_step = 0;
-  auto issue_next = [&](Tile<N>& t) -> bool {
-    bool real = false;
-    if (iq_rel == 0) {
-      issue_step<DT, D, BS>(t, prm, cur, ids_cur, iq_step, w, koff, voff);
-      real = true;
-      if (++iq_step == cur.niter) { iq_rel = 1; iq_step = 0; }
-    } else if (iq_rel == 1 && k_cur + 1 < nmine) {
-      issue_step<DT, D, BS>(t, prm, nxt, ids_nxt, iq_step, w, koff, voff);
-      real = true;
-      if (++iq_step == nxt.niter) { iq_rel = 2; iq_step = 0; }
-    } else {
-      // keep the per-slot load count fixed: a zero-length resource reads nothing
-      load_tile<N>(t, make_rsrc(prm.k_cache, 0), make_rsrc(prm.v_cache, 0), koff, voff, 0);
-    }
-    return real;
-  };
-
-  // compute one slot; returns true when this workgroup's work is finished
-  auto step = [&](Tile<N>& t, bool real) -> bool {
-    if (!real) return false;
-    const int valid = step_valid(prm, cur, ids_cur, i_cur, w);
-    if (valid > 0) attend_subtile<DT, N, kMM>(t, q_cur, valid, scale_log2, r, st, kst);
-    if (++i_cur < cur.niter) return false;
-    merge_item<DT, D, kMM>(sm, st, prm, w, lane, cur.s, cur.h, cur.p, cur.nparts);
-    st.reset();
-    if (++k_cur >= nmine) return true;
-    cur = nxt;
-    ids_cur = ids_nxt;
-#pragma unroll
-    for (int kk = 0; kk < N; ++kk) q_cur[kk] = q_nxt[kk];
-    i_cur = 0;
-    iq_rel -= 1;
-    if (k_cur + 1 < nmine) {
-      nxt = item_at(k_cur + 1);
-      ids_nxt = load_ids<BS>(prm, nxt, w, lane);
-      load_query<N>(q_nxt, prm.q, nxt.s, nxt.h, G, Hq, lane);
-    }
-    return false;
-  };
-
-  Tile<N> t0, t1, t2;
-  bool r0 = issue_next(t0);
-  bool r1 = issue_next(t1);
-  bool r2;
-  for (;;) {
-    r2 = issue_next(t2);
-    if (step(t0, r0)) break;
-    r0 = issue_next(t0);
-    if (step(t1, r1)) break;
-    r1 = issue_next(t1);
-    if (step(t2, r2)) break;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Grid kernel: one workgroup per possible item (any batch size).
+// Grid kernel: one workgroup per possible item (batches above kMaxStreamSeqs).
 // ---------------------------------------------------------------------------
 
 template <int DT, int D, int BS>
@@ -746,51 +632,352 @@ __global__ __launch_bounds__(64) void attn_reduce_kernel(AttnParams prm) {
   for (int j = 0; j < kPer; ++j) store_out<DT>(prm.out, orow + lane + 64 * j, o[j] * inv);
 }
 
-template <int DT, int D, int BS>
-hipError_t launch_typed(const AttnParams& prm, int persistent_wgs, hipStream_t stream) {
-  const dim3 block(kThreads);
-  if (persistent_wgs > 0 && prm.num_seqs <= kMaxPersistentSeqs) {
-    hipLaunchKernelGGL((attn_persistent_kernel<DT, D, BS>), dim3((unsigned)persistent_wgs), block,
-                       0, stream, prm);
-  } else {
-    const long long nwg = (long long)prm.num_seqs * prm.num_kv_heads * prm.max_partitions;
-    if (nwg <= 0) return hipSuccess;
-    if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_grid_kernel<DT, D, BS>), dim3((unsigned)nwg), block, 0, stream, prm);
+// ===========================================================================
+// Stream path
+// ===========================================================================
+
+// Where a global position lies: kv head h, sequence s, and the global
+// positions [A, E) of that (head, sequence)'s sub-tiles.  sS is the LDS prefix
+// of sub-tile counts (sS[s] = sub-tiles of sequences 0..s-1, sS[B] = nsub),
+// so sequence s owns [h*nsub + sS[s], h*nsub + sS[s+1]).  Wave-uniform.
+struct SeqSpan {
+  int h, s;
+  long long A, E;
+};
+
+__device__ __forceinline__ SeqSpan locate(long long p, int nsub, const int* sS, int B) {
+  SeqSpan sp;
+  sp.h = (int)(p / nsub);
+  const int rr = (int)(p - (long long)sp.h * nsub);
+  // largest s with sS[s] <= rr: skips empty sequences, which own no position
+  int a = 0, b = B - 1;
+  while (a < b) {
+    const int mid = (a + b + 1) >> 1;
+    if (uniform(sS[mid]) <= rr) a = mid; else b = mid - 1;
   }
+  sp.s = a;
+  const long long base = (long long)sp.h * nsub;
+  sp.A = base + uniform(sS[a]);
+  sp.E = base + uniform(sS[a + 1]);
+  return sp;
+}
+
+// Sub-tiles per wave: an equal share of every position, at least kMinChunk.
+__device__ __forceinline__ long long stream_chunk(long long total, int waves) {
+  const long long c = (total + waves - 1) / waves;
+  return c < kMinChunk ? kMinChunk : c;
+}
+
+// 64 block ids of sequence s starting at its logical block blk0 (lane i holds
+// block blk0 + i, -1 past the sequence's last block).
+__device__ __forceinline__ int load_id_batch(const AttnParams& prm, int s, int blk0, int nblk,
+                                             int lane) {
+  const int j = blk0 + lane;
+  return j < nblk ? prm.block_tables[(size_t)s * prm.max_blocks_per_seq + j] : -1;
+}
+
+template <int DT, int D, int BS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_stream_kernel(AttnParams prm) {
+  using Geo = Geometry<DT, D, BS>;
+  constexpr int N = Geo::N;
+  constexpr int kMM = Geo::kMM;
+  __shared__ int sS[kMaxStreamSeqs + 1];
+  __shared__ int sCtx[kMaxStreamSeqs];
+  __shared__ int sScan[kWaves];
+  __shared__ __attribute__((aligned(16))) char sK[kWaves][kSub * Geo::kRow];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int r = lane >> 4;
+  const int B = prm.num_seqs;
+  const int G = prm.group;
+  const int Hq = prm.num_q_heads;
+
+  // ---- sub-tile prefix over the batch (every workgroup, in LDS) -------------
+  const int per = (B + kThreads - 1) / kThreads;
+  int mine = 0;
+  for (int k = 0; k < per; ++k) {
+    const int s = tid * per + k;
+    if (s < B) {
+      int c = prm.context_lens[s];
+      c = c < 0 ? 0 : (c > prm.max_context_len ? prm.max_context_len : c);
+      sCtx[s] = c;
+      mine += (c + kSub - 1) / kSub;
+    }
+  }
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) sScan[w] = incl;
+  __syncthreads();
+  int run = incl - mine;
+  for (int ww = 0; ww < w; ++ww) run += sScan[ww];
+  for (int k = 0; k < per; ++k) {
+    const int s = tid * per + k;
+    if (s < B) {
+      sS[s] = run;
+      run += (sCtx[s] + kSub - 1) / kSub;
+    }
+  }
+  if (tid == 0) sS[B] = sScan[0] + sScan[1] + sScan[2] + sScan[3];
+  __syncthreads();
+  if (blockIdx.x == 0)  // for the merge kernel
+    for (int s = tid; s <= B; s += kThreads) prm.seq_prefix[s] = sS[s];
+
+  // ---- this wave's chunk of positions ---------------------------------------
+  const int nsub = uniform(sS[B]);
+  const long long total = (long long)prm.num_kv_heads * nsub;
+  const int waves = (int)gridDim.x * kWaves;
+  const long long chunk = stream_chunk(total, waves);
+  const int wv = xcd_remap(blockIdx.x, gridDim.x) * kWaves + w;
+  const long long a = (long long)wv * chunk;
+  const long long b = a + chunk < total ? a + chunk : total;
+  if (a >= b) return;  // no block-wide barrier follows
+
+  const int koff = 16 * lane;
+  const int voff = (4 * r) * Geo::kRow + (lane & 15) * (4 * N);
+  char* kst = sK[w];
+  const float scale_log2 = prm.scale_log2;
+
+  // ---- issue cursor: next position whose tiles are loaded ---------------------
+  long long pi = a;
+  SeqSpan si;
+  int nblk_i = 0, blk0_i = 0, ids_i = -1;
+  auto enter_issue = [&]() {
+    si = locate(pi, nsub, sS, B);
+    nblk_i = (uniform(sCtx[si.s]) + BS - 1) / BS;
+    blk0_i = (int)(pi - si.A) * kSub / BS;
+    ids_i = load_id_batch(prm, si.s, blk0_i, nblk_i, lane);
+  };
+  auto issue = [&](Tile<N>& t) {
+    if (pi < b) {
+      const int tsub = (int)(pi - si.A);
+      const int blk = tsub * kSub / BS;
+      if (blk - blk0_i >= 64) {
+        blk0_i = blk;
+        ids_i = load_id_batch(prm, si.s, blk0_i, nblk_i, lane);
+      }
+      int phys = __builtin_amdgcn_readlane(ids_i, blk - blk0_i);
+      const bool ok = (unsigned)phys < (unsigned)prm.num_blocks;
+      phys = ok ? phys : 0;
+      const size_t tile = ((size_t)phys * prm.num_kv_heads + si.h) * Geo::kTileBytes;
+      const int soff = (tsub * kSub % BS) * Geo::kRow;
+      const int nrec = ok ? Geo::kTileBytes : 0;  // a block id outside the pool reads zeros
+      load_tile<N>(t, make_rsrc(static_cast<const char*>(prm.k_cache) + tile, nrec),
+                   make_rsrc(static_cast<const char*>(prm.v_cache) + tile, nrec), koff, voff, soff);
+      ++pi;
+      if (pi == si.E && pi < b) enter_issue();
+    } else {
+      // past the chunk: keep the per-slot load count fixed, touch no memory
+      load_tile<N>(t, make_rsrc(prm.k_cache, 0), make_rsrc(prm.v_cache, 0), koff, voff, 0);
+    }
+  };
+
+  // ---- compute cursor: next position to attend --------------------------------
+  long long pc = a, p0 = a;
+  SeqSpan sc;
+  int ctx_c = 0;
+  uint4 qb[N];
+  WaveState<kMM> st;
+  auto enter_compute = [&]() {
+    sc = locate(pc, nsub, sS, B);
+    ctx_c = uniform(sCtx[sc.s]);
+    p0 = pc;
+    load_query<N>(qb, prm.q, sc.s, sc.h, G, Hq, lane);
+    st.reset();
+  };
+  // Finish the piece [p0, pc) of (sc.h, sc.s): the whole sequence goes to
+  // `out`; a piece of one to partial slot 0 (it starts the chunk) or 1.
+  auto finish_piece = [&]() {
+    float l = st.l + __shfl_xor(st.l, 16);
+    l += __shfl_xor(l, 32);
+    const int g = lane & 15;
+    if (g < G) {
+      float o[D / 4];
+      lane_run<D, kMM>(o, st);
+      const size_t row = (size_t)sc.s * Hq + (size_t)sc.h * G + g;
+      if (p0 == sc.A && pc == sc.E) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+        for (int i = 0; i < D / 4; ++i) o[i] *= inv;
+        store_run<DT, D>(static_cast<char*>(prm.out) + (row * D + r * (D / 4)) * Geo::EB, o);
+      } else {
+        const size_t slot = (size_t)wv * 2 + (p0 == a ? 0 : 1);
+        store_run<DT_F32, D>(prm.part_o + (slot * G + g) * D + r * (D / 4), o);
+        if (r == 0) *reinterpret_cast<float2*>(prm.part_ml + (slot * G + g) * 2) = make_float2(st.m, l);
+      }
+    }
+  };
+  auto step = [&](Tile<N>& t) {
+    const int tsub = (int)(pc - sc.A);
+    int valid = ctx_c - tsub * kSub;
+    valid = valid > kSub ? kSub : valid;
+    attend_subtile<DT, N, kMM>(t, qb, valid, scale_log2, r, st, kst);
+    ++pc;
+    if (pc == sc.E || pc == b) {
+      finish_piece();
+      if (pc < b) enter_compute();
+    }
+  };
+
+  enter_issue();
+  enter_compute();
+  Tile<N> t0, t1, t2;
+  issue(t0);
+  issue(t1);
+  for (;;) {
+    issue(t2);
+    step(t0);
+    if (pc >= b) break;
+    issue(t0);
+    step(t1);
+    if (pc >= b) break;
+    issue(t1);
+    step(t2);
+    if (pc >= b) break;
+  }
+}
+
+// Merge of the pieces of one split (sequence, query head): one wave, lanes
+// over the head dim, pieces visited in logical order.  Also writes the zero
+// row of an empty context.
+template <int DT, int D>
+__global__ __launch_bounds__(64) void attn_stream_merge_kernel(AttnParams prm) {
+  const int lane = threadIdx.x;
+  const int Hq = prm.num_q_heads;
+  const int G = prm.group;
+  const int s = blockIdx.x / Hq;
+  const int hq = blockIdx.x % Hq;
+  const int h = hq / G, g = hq % G;
+  constexpr int kPer = D / 64;
+  const size_t orow = ((size_t)s * Hq + hq) * D;
+  int ctx = prm.context_lens[s];
+  ctx = ctx < 0 ? 0 : (ctx > prm.max_context_len ? prm.max_context_len : ctx);
+  if (ctx == 0) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) store_out<DT>(prm.out, orow + lane + 64 * j, 0.f);
+    return;
+  }
+  const int nsub = prm.seq_prefix[prm.num_seqs];
+  const long long total = (long long)prm.num_kv_heads * nsub;
+  const long long chunk = stream_chunk(total, prm.stream_wgs * kWaves);
+  const long long A = (long long)h * nsub + prm.seq_prefix[s];
+  const long long E = A + (ctx + kSub - 1) / kSub;
+  const long long j1 = A / chunk, j2 = (E - 1) / chunk;
+  if (j1 == j2) return;  // one wave covered it and wrote `out`
+  const int npieces = (int)(j2 - j1 + 1);
+  // piece k: wave j1 + k; the first one sits in slot 1 unless it starts its chunk
+  auto slot_of = [&](int k) -> size_t {
+    const long long j = j1 + k;
+    return (size_t)j * 2 + ((k == 0 && A != j1 * chunk) ? 1 : 0);
+  };
+
+  float M = kNegInf;
+  for (int k = lane; k < npieces; k += 64) M = fmaxf(M, prm.part_ml[(slot_of(k) * G + g) * 2]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+
+  float o[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) o[j] = 0.f;
+  float lsum = 0.f;
+  for (int k = 0; k < npieces; ++k) {
+    const size_t sl = slot_of(k) * G + g;
+    const float2 ml = *reinterpret_cast<const float2*>(prm.part_ml + sl * 2);
+    const float f = ml.x == kNegInf ? 0.f : fast_exp2(ml.x - M);
+    lsum += f * ml.y;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) o[j] += f * prm.part_o[sl * D + lane + 64 * j];
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) store_out<DT>(prm.out, orow + lane + 64 * j, o[j] * inv);
+}
+
+// ===========================================================================
+// Launch
+// ===========================================================================
+
+template <int DT, int D, int BS>
+hipError_t launch_typed(const AttnParams& prm, hipStream_t stream) {
+  const dim3 block(kThreads);
+  const long long nout = (long long)prm.num_seqs * prm.num_q_heads;
+  if (nout > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (prm.stream_wgs > 0) {
+    hipLaunchKernelGGL((attn_stream_kernel<DT, D, BS>), dim3((unsigned)prm.stream_wgs), block, 0,
+                       stream, prm);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((attn_stream_merge_kernel<DT, D>), dim3((unsigned)nout), dim3(64), 0,
+                       stream, prm);
+    return hipGetLastError();
+  }
+  const long long nwg = (long long)prm.num_seqs * prm.num_kv_heads * prm.max_partitions;
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((attn_grid_kernel<DT, D, BS>), dim3((unsigned)nwg), block, 0, stream, prm);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || prm.max_partitions <= 1) return err;
-  hipLaunchKernelGGL((attn_reduce_kernel<DT, D>), dim3((unsigned)(prm.num_seqs * prm.num_q_heads)),
-                     dim3(64), 0, stream, prm);
+  hipLaunchKernelGGL((attn_reduce_kernel<DT, D>), dim3((unsigned)nout), dim3(64), 0, stream, prm);
   return hipGetLastError();
 }
 
 template <int DT, int D>
-hipError_t launch_bs(const AttnParams& prm, int bs, int persistent_wgs, hipStream_t stream) {
+hipError_t launch_bs(const AttnParams& prm, int bs, hipStream_t stream) {
   switch (bs) {
-    case 16: return launch_typed<DT, D, 16>(prm, persistent_wgs, stream);
-    case 32: return launch_typed<DT, D, 32>(prm, persistent_wgs, stream);
+    case 16: return launch_typed<DT, D, 16>(prm, stream);
+    case 32: return launch_typed<DT, D, 32>(prm, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int DT>
-hipError_t launch_d(const AttnParams& prm, int d, int bs, int persistent_wgs, hipStream_t stream) {
+hipError_t launch_d(const AttnParams& prm, int d, int bs, hipStream_t stream) {
   switch (d) {
-    case 64: return launch_bs<DT, 64>(prm, bs, persistent_wgs, stream);
-    case 128: return launch_bs<DT, 128>(prm, bs, persistent_wgs, stream);
+    case 64: return launch_bs<DT, 64>(prm, bs, stream);
+    case 128: return launch_bs<DT, 128>(prm, bs, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 }  // namespace
 
+AttnWorkspace attn_workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_context_len, int32_t stream_wgs) {
+  AttnWorkspace ws{0, 0, 0, 0};
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return ws;
+  if (stream_wgs > 0) {
+    const size_t G = (size_t)(num_q_heads / num_kv_heads);
+    const size_t slots = (size_t)stream_wgs * kWaves * 2;
+    ws.prefix_off = 0;
+    ws.part_o_off = align256(sizeof(int32_t) * ((size_t)num_seqs + 1));
+    ws.part_ml_off = align256(ws.part_o_off + slots * G * head_dim * sizeof(float));
+    ws.bytes = ws.part_ml_off + slots * G * 2 * sizeof(float);
+    return ws;
+  }
+  const int32_t P = max_context_len <= 0 ? 1
+                                          : (max_context_len + kPartitionTokens - 1) / kPartitionTokens;
+  if (P <= 1) return ws;
+  const size_t rows = (size_t)num_seqs * num_q_heads * P;
+  ws.part_o_off = 0;
+  ws.part_ml_off = rows * head_dim * sizeof(float);
+  ws.bytes = ws.part_ml_off + rows * 2 * sizeof(float);
+  return ws;
+}
+
 hipError_t launch_paged_attention(const AttnParams& prm, int dtype, int head_dim,
-                                  int block_size, int persistent_wgs, hipStream_t stream) {
+                                  int block_size, hipStream_t stream) {
   switch (dtype) {
-    case DT_F32: return launch_d<DT_F32>(prm, head_dim, block_size, persistent_wgs, stream);
-    case DT_F16: return launch_d<DT_F16>(prm, head_dim, block_size, persistent_wgs, stream);
-    case DT_BF16: return launch_d<DT_BF16>(prm, head_dim, block_size, persistent_wgs, stream);
+    case DT_F32: return launch_d<DT_F32>(prm, head_dim, block_size, stream);
+    case DT_F16: return launch_d<DT_F16>(prm, head_dim, block_size, stream);
+    case DT_BF16: return launch_d<DT_BF16>(prm, head_dim, block_size, stream);
     default: return hipErrorInvalidValue;
   }
 }

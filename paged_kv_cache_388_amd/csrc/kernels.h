@@ -9,14 +9,26 @@
 
 namespace pkv {
 
-// Tokens per split-context partition.  A multiple of every supported block
-// size, so partitions start on block boundaries.
+// Tokens per MFMA sub-tile: the unit of work of the decode kernels.
+constexpr int kSubTokens = 16;
+
+// ---- stream path (default) -------------------------------------------------
+// Workgroups of 4 independent waves, two per compute unit.  The work of one
+// call is the ordered list of (kv head, sequence, 16-token sub-tile)
+// positions; wave v of the grid takes positions [v * chunk, (v + 1) * chunk).
+// A wave finishes each sequence piece it covers: a whole sequence is written
+// straight to `out`, a piece of one to one of the wave's two partial slots,
+// merged afterwards in logical order.
+constexpr int kStreamWaves = 4;           // waves per workgroup
+constexpr int kMaxStreamSeqs = 4096;      // batch limit (per-sequence tables live in LDS)
+constexpr int kMinChunk = 4;              // sub-tiles per wave at least
+
+// ---- grid path (batches above kMaxStreamSeqs) --------------------------------
+// One workgroup per (kv head, sequence, partition of kPartitionTokens tokens).
 constexpr int kPartitionTokens = 512;
 
 struct AttnParams {
   void* out;                    // [B, H_q, D] pool dtype
-  float* part_o;                // [B, H_q, P, D] fp32 unnormalised partition outputs
-  float* part_ml;               // [B, H_q, P, 2] fp32 (max logit in log2 units, normaliser)
   const void* q;                // [B, H_q, D]
   const void* k_cache;          // [NB, H_kv, bs, D]
   const void* v_cache;
@@ -29,20 +41,29 @@ struct AttnParams {
   int32_t group;                // H_q / H_kv
   int32_t num_blocks;
   int32_t max_context_len;
-  int32_t max_partitions;       // ceil(max_context_len / kPartitionTokens), >= 1
   float scale_log2;             // scale * log2(e): logits kept in base-2 units
+  // Workspace views.  Stream path: part_o [2 * waves, G, D], part_ml
+  // [2 * waves, G, 2] (max logit in log2 units, normaliser), seq_prefix
+  // [B + 1] (sub-tiles of the sequences before each one).  Grid path: part_o
+  // [B, H_q, P, D], part_ml [B, H_q, P, 2], seq_prefix unused.
+  float* part_o;
+  float* part_ml;
+  int32_t* seq_prefix;
+  int32_t stream_wgs;           // > 0: stream path with this many workgroups
+  int32_t max_partitions;       // grid path: ceil(max_context_len / kPartitionTokens)
 };
 
-// Largest batch the persistent attention kernel takes (its work list lives in
-// LDS); larger batches use the grid kernel.
-constexpr int kMaxPersistentSeqs = 2048;
+// Workspace layout of one decode call, shared by the size query and the call.
+struct AttnWorkspace {
+  size_t prefix_off, part_o_off, part_ml_off, bytes;
+};
+AttnWorkspace attn_workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_context_len, int32_t stream_wgs);
 
-// dtype: 0 f32, 1 f16, 2 bf16.  persistent_wgs: workgroups of the persistent
-// kernel (a multiple of 8), or 0 for the grid kernel.  Returns
-// hipErrorInvalidValue for a (dtype, head_dim, block_size) combination that
-// is not instantiated.
+// dtype: 0 f32, 1 f16, 2 bf16.  Returns hipErrorInvalidValue for a (dtype,
+// head_dim, block_size) combination that is not instantiated.
 hipError_t launch_paged_attention(const AttnParams& p, int dtype, int head_dim,
-                                  int block_size, int persistent_wgs, hipStream_t stream);
+                                  int block_size, hipStream_t stream);
 
 hipError_t launch_kv_append(const void* key, const void* value, void* k_cache,
                             void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,

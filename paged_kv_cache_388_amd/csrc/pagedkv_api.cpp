@@ -5,7 +5,6 @@
 
 #include <stdarg.h>
 #include <stdio.h>
-#include <stdlib.h>
 
 #include <atomic>
 
@@ -56,16 +55,9 @@ size_t pool_block_bytes(const pkv_pool& pool) {
   return (size_t)pool.num_kv_heads * pool.block_size * pool.head_dim * elem_bytes(pool.dtype);
 }
 
-// Workgroups of the persistent attention kernel on the current device: two
-// per compute unit (its occupancy), rounded down to a multiple of the 8 XCDs.
-// The grid kernel is the default; PAGEDKV_PERSISTENT=1 selects the persistent
-// one (read once per process).
-int persistent_workgroups() {
-  static const bool enabled = [] {
-    const char* e = getenv("PAGEDKV_PERSISTENT");
-    return e && atoi(e) == 1;
-  }();
-  if (!enabled) return 0;
+// Workgroups of the stream attention kernel on the current device: two per
+// compute unit (its occupancy), a multiple of the 8 XCDs.  Cached per device.
+int stream_workgroups() {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cached[kMaxDevices];
   int dev = 0;
@@ -75,10 +67,16 @@ int persistent_workgroups() {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     wgs = (2 * cus) / 8 * 8;
-    if (wgs <= 0) wgs = -1;
+    if (wgs < 8) wgs = 8;
     cached[dev].store(wgs, std::memory_order_relaxed);
   }
-  return wgs > 0 ? wgs : 0;
+  return wgs;
+}
+
+// Workgroups of the stream path for this batch on the current device, or 0
+// for the grid path (batches above kMaxStreamSeqs).
+int32_t stream_wgs_for(int32_t num_seqs) {
+  return num_seqs <= pkv::kMaxStreamSeqs ? stream_workgroups() : 0;
 }
 
 int32_t partitions_for(int32_t max_context_len) {
@@ -126,12 +124,15 @@ pkv_status paged_kv_append(const void* key, const void* value, void* k_cache, vo
   return err == hipSuccess ? PKV_OK : hip_fail(err, "paged_kv_append launch");
 }
 
-size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+size_t paged_attention_workspace_bytes(pkv_pool pool, int32_t num_seqs, int32_t num_q_heads,
                                        int32_t max_context_len) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
-  const int32_t P = partitions_for(max_context_len);
-  if (P <= 1) return 0;
-  return (size_t)num_seqs * num_q_heads * P * (size_t)(head_dim + 2) * sizeof(float);
+  if (check_pool(pool) != PKV_OK || num_seqs <= 0 || num_q_heads <= 0 || max_context_len < 0 ||
+      num_q_heads % pool.num_kv_heads != 0)
+    return 0;
+  g_err[0] = '\0';
+  return pkv::attn_workspace_layout(num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim,
+                                    max_context_len, stream_wgs_for(num_seqs))
+      .bytes;
 }
 
 pkv_status paged_attention_decode(void* out, const void* q, const void* k_cache,
@@ -159,11 +160,12 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_cache,
     return fail(PKV_EINVAL, "null pointer argument");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_EINVAL, "out, q and the pools must be 16-byte aligned");
-  const size_t need = paged_attention_workspace_bytes(num_seqs, num_q_heads, pool.head_dim,
-                                                      max_context_len);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(PKV_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
-  if (need > 0 && !aligned16(workspace)) return fail(PKV_EINVAL, "workspace must be 16-byte aligned");
+  const int32_t stream_wgs = stream_wgs_for(num_seqs);
+  const pkv::AttnWorkspace lay = pkv::attn_workspace_layout(
+      num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim, max_context_len, stream_wgs);
+  if (lay.bytes > 0 && (!workspace || workspace_bytes < lay.bytes))
+    return fail(PKV_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, lay.bytes);
+  if (lay.bytes > 0 && !aligned16(workspace)) return fail(PKV_EINVAL, "workspace must be 16-byte aligned");
 
   pkv::AttnParams prm;
   prm.out = out;
@@ -179,13 +181,14 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_cache,
   prm.group = group;
   prm.num_blocks = pool.num_blocks;
   prm.max_context_len = max_context_len;
-  prm.max_partitions = partitions_for(max_context_len);
   prm.scale_log2 = scale * 1.4426950408889634f;
-  const size_t po = (size_t)num_seqs * num_q_heads * prm.max_partitions * pool.head_dim;
-  prm.part_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
-  prm.part_ml = need > 0 ? static_cast<float*>(workspace) + po : nullptr;
-  hipError_t err = pkv::launch_paged_attention(prm, pool.dtype, pool.head_dim, pool.block_size,
-                                               persistent_workgroups(), stream);
+  char* base = static_cast<char*>(workspace);
+  prm.seq_prefix = lay.bytes > 0 ? reinterpret_cast<int32_t*>(base + lay.prefix_off) : nullptr;
+  prm.part_o = lay.bytes > 0 ? reinterpret_cast<float*>(base + lay.part_o_off) : nullptr;
+  prm.part_ml = lay.bytes > 0 ? reinterpret_cast<float*>(base + lay.part_ml_off) : nullptr;
+  prm.stream_wgs = stream_wgs;
+  prm.max_partitions = partitions_for(max_context_len);
+  hipError_t err = pkv::launch_paged_attention(prm, pool.dtype, pool.head_dim, pool.block_size, stream);
   return err == hipSuccess ? PKV_OK : hip_fail(err, "paged_attention_decode launch");
 }
 

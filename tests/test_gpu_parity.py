@@ -178,12 +178,27 @@ def test_caller_stream_is_used():
     check_attention(to_host(out, "f16"), oracle_step(w), "f16", "side stream")
 
 
-def test_large_batch_uses_grid_kernel_path():
-    # more sequences than the persistent kernel's LDS work list holds
+def test_large_batch_stream_path():
     rng = np.random.default_rng(12)
     ctx = rng.integers(0, 700, size=2100)
     w = wl.build("bigbatch", 12, rng, ctx, 4, 2, 64, 16, "bf16")
     _run_and_check(w, "B=2100")
+
+
+def test_batch_above_stream_limit_uses_grid_path():
+    # more sequences than the stream kernel's LDS tables hold: one workgroup per
+    # (kv head, sequence, 512-token partition) and a partition merge
+    rng = np.random.default_rng(14)
+    ctx = rng.integers(0, 40, size=4200)
+    ctx[::97] = rng.integers(513, 1600, size=len(ctx[::97]))
+    w = wl.build("gridpath", 14, rng, ctx, 8, 2, 64, 16, "f16", poison=True)
+    print(f"[gpu] grid path: B={w.num_seqs}", flush=True)
+    dw = DeviceWorkload(w)
+    out = to_host(dw.step(), "f16")
+    torch.cuda.synchronize()
+    sample = sorted(set(range(0, 4200, 97)) | set(np.random.default_rng(15).choice(4200, 150).tolist()))
+    ref = oracle_step(w, seq_ids=sample)
+    check_attention(out[sample], ref, "f16", "grid path sample")
 
 
 def test_single_sequence_many_partitions():

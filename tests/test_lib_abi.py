@@ -44,11 +44,18 @@ def test_every_declared_symbol_is_exported(lib):
 def test_partition_and_workspace_arithmetic(lib):
     assert lib.pkv_partition_tokens() == 512
     f = lib.paged_attention_workspace_bytes
-    assert f(4, 2, 64, 70) == 0                      # one partition: no workspace
-    assert f(4, 2, 64, 512) == 0
-    assert f(4, 2, 64, 513) == 4 * 2 * 2 * (64 + 2) * 4
-    assert f(32, 64, 128, 32768) == 32 * 64 * 64 * 130 * 4
-    assert f(0, 2, 64, 1000) == 0 and f(4, 2, 64, -1) == 0
+    p = _pool(nb=8, hkv=2, bs=16, d=64)
+    # above 4096 sequences: fp32 states of every (sequence, query head, 512-token partition)
+    assert f(p, 5000, 4, 512) == 0                                  # one partition: none
+    assert f(p, 5000, 4, 513) == 5000 * 4 * 2 * (64 + 2) * 4
+    assert f(_pool(hkv=8, d=128), 5000, 64, 32768) == 5000 * 64 * 64 * 130 * 4
+    # invalid input
+    assert f(p, 0, 4, 1000) == 0 and f(p, 4, 4, -1) == 0 and f(p, 4, 3, 100) == 0
+    assert f(_pool(bs=8), 4, 4, 100) == 0
+    # up to 4096 sequences the size depends on the device's CU count (none here: the
+    # grid layout applies) but never on the context lengths once a device is present
+    small = [f(p, 4, 4, n) for n in (70, 513, 100000)]
+    assert (small[0] == 0 and small[1] == 4 * 4 * 2 * (64 + 2) * 4) or (small[0] == small[1] == small[2] > 0)
 
 
 def test_status_strings(lib):
@@ -57,11 +64,13 @@ def test_status_strings(lib):
     assert lib.pkv_last_error() == b""
 
 
+FAKE = ctypes.c_void_p(0x1000)  # aligned, never dereferenced: validation fails first
+
+
 def _pool(nb=8, hkv=2, bs=16, d=64, dtype=_lib.PKV_BF16):
     return _lib.PkvPool(nb, hkv, bs, d, dtype)
 
 
-FAKE = ctypes.c_void_p(0x1000)  # aligned, never dereferenced: validation fails first
 
 
 @pytest.mark.parametrize("pool,code", [
