@@ -114,13 +114,14 @@ PKV_API size_t paged_attention_workspace_bytes(pkv_pool pool, int32_t num_seqs,
  * over logical tokens t < n; token t lives in physical block
  * block_tables[s, t / block_size] at offset t % block_size.  n = 0 gives a
  * zero row.  Softmax and accumulation are fp32; out is rounded to nearest
- * even in the pool dtype.  The context is cut into 16-token sub-tiles; each
- * wave of the kernel walks an equal run of them, and where a sequence's
- * context is split between waves their partial states (running max,
- * normaliser, unnormalised output) are merged exactly by a log-sum-exp
- * rescale.  The split points depend only on the context lengths, and every
- * reduction runs in logical token order, so the result is bit-identical under
- * any physical placement of the blocks and across repeated calls.  A block id
+ * even in the pool dtype.  The context is cut into 16-token sub-tiles and
+ * the call's sub-tiles into equal chunks, one per wave of the kernel; where a
+ * sequence's context spans several chunks, their partial states (running
+ * max, normaliser, unnormalised output) are merged exactly by a log-sum-exp
+ * rescale.  The chunk boundaries depend only on the context lengths and the
+ * device's compute-unit count, and every reduction runs in logical token
+ * order, so the result is bit-identical under any physical placement of the
+ * blocks and across repeated calls.  A block id
  * outside the pool is never dereferenced (its tokens read as zeros).
  *
  *   out           [num_seqs, num_q_heads, head_dim]  pool dtype, written
@@ -135,9 +136,9 @@ PKV_API size_t paged_attention_workspace_bytes(pkv_pool pool, int32_t num_seqs,
  *                 max_blocks_per_seq * block_size must be >= it
  *   workspace     device buffer of >= paged_attention_workspace_bytes(pool,
  *                 num_seqs, num_q_heads, max_context_len) bytes, 16-byte
- *                 aligned (may be NULL when that is 0); contents are scratch,
- *                 need no initialisation and must not be shared by calls
- *                 that can run concurrently
+ *                 aligned (may be NULL when that is 0); scratch, needs no
+ *                 initialisation.  Calls that can run concurrently must not
+ *                 share it.
  */
 PKV_API pkv_status paged_attention_decode(void* out, const void* q,
                                           const void* k_cache, const void* v_cache,

@@ -65,6 +65,7 @@ typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));  // cvt_pkrtz result
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kStreamWaves;  // waves per workgroup, both paths
 constexpr int kThreads = 64 * kWaves;
@@ -138,27 +139,26 @@ struct Tile {
   uint32_t v[4][N];
 };
 
-// voff: this lane's V byte offset inside a 16-token sub-tile (K uses
-// 16*lane); soff: byte offset of the sub-tile inside its (block, head) tile.
+// koff / voff: this lane's K / V byte offsets inside a 16-token sub-tile
+// (the resources start at the sub-tile).
 template <int N>
-__device__ __forceinline__ void load_tile(Tile<N>& t, rsrc_t kr, rsrc_t vr, int koff, int voff,
-                                          int soff) {
+__device__ __forceinline__ void load_tile(Tile<N>& t, rsrc_t kr, rsrc_t vr, int koff, int voff) {
   constexpr int kRow = 16 * 4 * N;  // bytes per token row = D * elem_bytes
 #pragma unroll
   for (int kk = 0; kk < N; ++kk)
     t.k[kk] = __builtin_bit_cast(
-        uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + kk * 1024, soff, kStreamPolicy));
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + kk * 1024, 0, kStreamPolicy));
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if constexpr (N == 2) {
       const uint2 x = __builtin_bit_cast(
-          uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, voff + e * kRow, soff, kStreamPolicy));
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, voff + e * kRow, 0, kStreamPolicy));
       t.v[e][0] = x.x; t.v[e][1] = x.y;
     } else {
 #pragma unroll
       for (int j = 0; j < N / 4; ++j) {
         const uint4 x = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + e * kRow + 16 * j, soff,
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + e * kRow + 16 * j, 0,
                                                          kStreamPolicy));
         t.v[e][4 * j + 0] = x.x; t.v[e][4 * j + 1] = x.y;
         t.v[e][4 * j + 2] = x.z; t.v[e][4 * j + 3] = x.w;
@@ -273,15 +273,8 @@ __device__ __forceinline__ void attend_subtile(Tile<N>& t, const uint4 (&qb)[N],
 #pragma unroll
   for (int mm = 0; mm < kMM; ++mm) st.acc[mm] *= alpha;
 
-  // ---- tail: V rows of masked tokens are zeroed (select, never 0 * v)
-  if (valid < kSub) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool keep = 4 * r + e < valid;
-#pragma unroll
-      for (int j = 0; j < N; ++j) t.v[e][j] = keep ? t.v[e][j] : 0u;
-    }
-  }
+  // Rows at or past `valid` were loaded as zeros (their buffer range ends at
+  // the last real token), so stale or NaN bits in unused slots never reach PV.
 
   // ---- PV on MFMA ----------------------------------------------------------
   if constexpr (DT == DT_F32) {
@@ -495,9 +488,10 @@ __device__ __forceinline__ int load_ids(const AttnParams& prm, const Item& it, i
 }
 
 
-// Issue the loads of step i of item `it` for wave w.  A step whose sub-tile
-// holds no token, or whose block id lies outside the pool, gets a zero-length
-// resource: its loads return zeros and touch no memory.
+// Issue the loads of step i of item `it` for wave w.  The buffer range of a
+// sub-tile ends at its last real token, so rows past the context (and a whole
+// sub-tile that holds no token or whose block id lies outside the pool) read
+// as zeros and touch no memory.
 template <int DT, int D, int BS>
 __device__ __forceinline__ void issue_step(Tile<Geometry<DT, D, BS>::N>& t, const AttnParams& prm,
                                            const Item& it, int ids, int i, int w, int koff, int voff) {
@@ -506,11 +500,13 @@ __device__ __forceinline__ void issue_step(Tile<Geometry<DT, D, BS>::N>& t, cons
   int phys = __builtin_amdgcn_readlane(ids, i);
   const bool ok = j < it.nsub && (unsigned)phys < (unsigned)prm.num_blocks;
   phys = ok ? phys : 0;
-  const size_t tile = ((size_t)phys * prm.num_kv_heads + it.h) * Geo::kTileBytes;
-  const int soff = ((it.tok0 + kSub * j) % BS) * Geo::kRow;
-  const int nrec = ok ? Geo::kTileBytes : 0;
-  load_tile<Geo::N>(t, make_rsrc(static_cast<const char*>(prm.k_cache) + tile, nrec),
-                    make_rsrc(static_cast<const char*>(prm.v_cache) + tile, nrec), koff, voff, soff);
+  int valid = it.ctx - (it.tok0 + kSub * j);
+  valid = valid > kSub ? kSub : valid;
+  const size_t sub = ((size_t)phys * prm.num_kv_heads + it.h) * Geo::kTileBytes +
+                     ((it.tok0 + kSub * j) % BS) * Geo::kRow;
+  const int nrec = ok ? valid * Geo::kRow : 0;
+  load_tile<Geo::N>(t, make_rsrc(static_cast<const char*>(prm.k_cache) + sub, nrec),
+                    make_rsrc(static_cast<const char*>(prm.v_cache) + sub, nrec), koff, voff);
 }
 
 // Tokens of step i of item `it` (for wave w) that are real: 0..16.
@@ -642,13 +638,13 @@ __global__ __launch_bounds__(64) void attn_reduce_kernel(AttnParams prm) {
 // so sequence s owns [h*nsub + sS[s], h*nsub + sS[s+1]).  Wave-uniform.
 struct SeqSpan {
   int h, s;
-  long long A, E;
+  int A, E;
 };
 
-__device__ __forceinline__ SeqSpan locate(long long p, int nsub, const int* sS, int B) {
+__device__ __forceinline__ SeqSpan locate(int p, int nsub, const int* sS, int B) {
   SeqSpan sp;
-  sp.h = (int)(p / nsub);
-  const int rr = (int)(p - (long long)sp.h * nsub);
+  sp.h = p / nsub;
+  const int rr = p - sp.h * nsub;
   // largest s with sS[s] <= rr: skips empty sequences, which own no position
   int a = 0, b = B - 1;
   while (a < b) {
@@ -656,17 +652,27 @@ __device__ __forceinline__ SeqSpan locate(long long p, int nsub, const int* sS, 
     if (uniform(sS[mid]) <= rr) a = mid; else b = mid - 1;
   }
   sp.s = a;
-  const long long base = (long long)sp.h * nsub;
+  const int base = sp.h * nsub;
   sp.A = base + uniform(sS[a]);
   sp.E = base + uniform(sS[a + 1]);
   return sp;
 }
 
-// Sub-tiles per wave: an equal share of every position, at least kMinChunk.
-__device__ __forceinline__ long long stream_chunk(long long total, int waves) {
-  const long long c = (total + waves - 1) / waves;
+// The position list [0, total) cut into one chunk per wave: wave v owns
+// [v * chunk, min((v + 1) * chunk, total)).  The cut depends only on total
+// and the grid, so every piece boundary, and with it the result, is fixed by
+// the context lengths.  total <= kMaxStreamPositions (the host routes larger
+// calls to the grid path).
+__device__ __forceinline__ int stream_chunk(int total, int waves) {
+  const int c = total / waves + (total % waves != 0);
   return c < kMinChunk ? kMinChunk : c;
 }
+
+// What the compute side needs to know about one issued sub-tile: its global
+// position (-1 for a bubble).  Wave-uniform.
+struct SlotMeta {
+  int p;
+};
 
 // 64 block ids of sequence s starting at its logical block blk0 (lane i holds
 // block blk0 + i, -1 past the sequence's last block).
@@ -729,14 +735,13 @@ void attn_stream_kernel(AttnParams prm) {
   if (blockIdx.x == 0)  // for the merge kernel
     for (int s = tid; s <= B; s += kThreads) prm.seq_prefix[s] = sS[s];
 
-  // ---- this wave's chunk of positions ---------------------------------------
+  // ---- this wave's chunk of positions -----------------------------------------
   const int nsub = uniform(sS[B]);
-  const long long total = (long long)prm.num_kv_heads * nsub;
-  const int waves = (int)gridDim.x * kWaves;
-  const long long chunk = stream_chunk(total, waves);
+  const int total = prm.num_kv_heads * nsub;
+  const int chunk = stream_chunk(total, (int)gridDim.x * kWaves);
   const int wv = xcd_remap(blockIdx.x, gridDim.x) * kWaves + w;
-  const long long a = (long long)wv * chunk;
-  const long long b = a + chunk < total ? a + chunk : total;
+  const int a = (int)min((long long)wv * chunk, (long long)total);
+  const int b = a + chunk < total ? a + chunk : total;
   if (a >= b) return;  // no block-wide barrier follows
 
   const int koff = 16 * lane;
@@ -745,55 +750,67 @@ void attn_stream_kernel(AttnParams prm) {
   const float scale_log2 = prm.scale_log2;
 
   // ---- issue cursor: next position whose tiles are loaded ---------------------
-  long long pi = a;
+  int pi = a;
   SeqSpan si;
-  int nblk_i = 0, blk0_i = 0, ids_i = -1;
-  auto enter_issue = [&]() {
-    si = locate(pi, nsub, sS, B);
-    nblk_i = (uniform(sCtx[si.s]) + BS - 1) / BS;
-    blk0_i = (int)(pi - si.A) * kSub / BS;
+  int ctx_i = 0, nblk_i = 0, blk0_i = 0, ids_i = -1;
+  // Block ids arrive in 64-entry batches.  The wait for a batch is taken
+  // where it is loaded (a sequence entry, or every 64 blocks): loads issued
+  // on some paths only would otherwise make the wait at every lookup drain
+  // the tiles in flight.
+  auto load_ids_now = [&]() {
     ids_i = load_id_batch(prm, si.s, blk0_i, nblk_i, lane);
+    asm volatile("" : "+v"(ids_i));
   };
-  auto issue = [&](Tile<N>& t) {
+  auto enter_issue_seq = [&]() {
+    si = locate(pi, nsub, sS, B);
+    ctx_i = uniform(sCtx[si.s]);
+    nblk_i = (ctx_i + BS - 1) / BS;
+    blk0_i = (pi - si.A) * kSub / BS;
+    load_ids_now();
+  };
+  auto issue = [&](Tile<N>& t, SlotMeta& m) {
     if (pi < b) {
-      const int tsub = (int)(pi - si.A);
+      m.p = pi;
+      // all wave-uniform; readfirstlane keeps them (and the resources built
+      // from them) in scalar registers
+      const int tsub = uniform(pi - si.A);
       const int blk = tsub * kSub / BS;
       if (blk - blk0_i >= 64) {
         blk0_i = blk;
-        ids_i = load_id_batch(prm, si.s, blk0_i, nblk_i, lane);
+        load_ids_now();
       }
       int phys = __builtin_amdgcn_readlane(ids_i, blk - blk0_i);
       const bool ok = (unsigned)phys < (unsigned)prm.num_blocks;
       phys = ok ? phys : 0;
-      const size_t tile = ((size_t)phys * prm.num_kv_heads + si.h) * Geo::kTileBytes;
-      const int soff = (tsub * kSub % BS) * Geo::kRow;
-      const int nrec = ok ? Geo::kTileBytes : 0;  // a block id outside the pool reads zeros
-      load_tile<N>(t, make_rsrc(static_cast<const char*>(prm.k_cache) + tile, nrec),
-                   make_rsrc(static_cast<const char*>(prm.v_cache) + tile, nrec), koff, voff, soff);
+      int valid = ctx_i - tsub * kSub;
+      valid = valid > kSub ? kSub : valid;
+      const size_t sub = ((size_t)phys * prm.num_kv_heads + uniform(si.h)) * Geo::kTileBytes +
+                         (tsub * kSub % BS) * Geo::kRow;
+      // the range ends at the last real token: later rows, and every row of a
+      // block id outside the pool, read as zeros without touching memory
+      const int nrec = uniform(ok ? valid * Geo::kRow : 0);
+      load_tile<N>(t, make_rsrc(static_cast<const char*>(prm.k_cache) + sub, nrec),
+                   make_rsrc(static_cast<const char*>(prm.v_cache) + sub, nrec), koff, voff);
       ++pi;
-      if (pi == si.E && pi < b) enter_issue();
+      if (pi < b && pi == si.E) enter_issue_seq();
     } else {
       // past the chunk: keep the per-slot load count fixed, touch no memory
-      load_tile<N>(t, make_rsrc(prm.k_cache, 0), make_rsrc(prm.v_cache, 0), koff, voff, 0);
+      m.p = -1;
+      load_tile<N>(t, make_rsrc(prm.k_cache, 0), make_rsrc(prm.v_cache, 0), koff, voff);
     }
   };
 
-  // ---- compute cursor: next position to attend --------------------------------
-  long long pc = a, p0 = a;
+  // ---- compute cursor -----------------------------------------------------------
+  // The open piece: positions [p0, ...) of sequence span sc.  A piece that
+  // does not cover its whole sequence sits in partial slot 0 of this wave if
+  // it starts the chunk, else in slot 1 (only the chunk's last piece can).
+  bool open = false;
+  int p0 = 0;
   SeqSpan sc;
   int ctx_c = 0;
   uint4 qb[N];
   WaveState<kMM> st;
-  auto enter_compute = [&]() {
-    sc = locate(pc, nsub, sS, B);
-    ctx_c = uniform(sCtx[sc.s]);
-    p0 = pc;
-    load_query<N>(qb, prm.q, sc.s, sc.h, G, Hq, lane);
-    st.reset();
-  };
-  // Finish the piece [p0, pc) of (sc.h, sc.s): the whole sequence goes to
-  // `out`; a piece of one to partial slot 0 (it starts the chunk) or 1.
-  auto finish_piece = [&]() {
+  auto finish_piece = [&](int p_end) {
     float l = st.l + __shfl_xor(st.l, 16);
     l += __shfl_xor(l, 32);
     const int g = lane & 15;
@@ -801,7 +818,7 @@ void attn_stream_kernel(AttnParams prm) {
       float o[D / 4];
       lane_run<D, kMM>(o, st);
       const size_t row = (size_t)sc.s * Hq + (size_t)sc.h * G + g;
-      if (p0 == sc.A && pc == sc.E) {
+      if (p0 == sc.A && p_end == sc.E) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
         for (int i = 0; i < D / 4; ++i) o[i] *= inv;
@@ -813,33 +830,49 @@ void attn_stream_kernel(AttnParams prm) {
       }
     }
   };
-  auto step = [&](Tile<N>& t) {
-    const int tsub = (int)(pc - sc.A);
+  auto step = [&](Tile<N>& t, const SlotMeta& m) {
+    if (!open) {
+      sc = locate(m.p, nsub, sS, B);
+      ctx_c = uniform(sCtx[sc.s]);
+      p0 = m.p;
+      load_query<N>(qb, prm.q, sc.s, sc.h, G, Hq, lane);
+      // Take the wait for the query here, where a piece opens: the loads are
+      // conditional, and a wait placed at their use would drain every
+      // sub-tile's prefetched loads on every step.
+#pragma unroll
+      for (int kk = 0; kk < N; ++kk) {
+        u32x4 qv = __builtin_bit_cast(u32x4, qb[kk]);
+        asm volatile("" : "+v"(qv));
+        qb[kk] = __builtin_bit_cast(uint4, qv);
+      }
+      st.reset();
+      open = true;
+    }
+    const int tsub = m.p - sc.A;
     int valid = ctx_c - tsub * kSub;
     valid = valid > kSub ? kSub : valid;
     attend_subtile<DT, N, kMM>(t, qb, valid, scale_log2, r, st, kst);
-    ++pc;
-    if (pc == sc.E || pc == b) {
-      finish_piece();
-      if (pc < b) enter_compute();
+    if (m.p + 1 == sc.E || m.p + 1 == b) {
+      finish_piece(m.p + 1);
+      open = false;
     }
   };
 
-  enter_issue();
-  enter_compute();
+  enter_issue_seq();
   Tile<N> t0, t1, t2;
-  issue(t0);
-  issue(t1);
+  SlotMeta m0, m1, m2;
+  issue(t0, m0);
+  issue(t1, m1);
   for (;;) {
-    issue(t2);
-    step(t0);
-    if (pc >= b) break;
-    issue(t0);
-    step(t1);
-    if (pc >= b) break;
-    issue(t1);
-    step(t2);
-    if (pc >= b) break;
+    issue(t2, m2);
+    if (m0.p < 0) break;
+    step(t0, m0);
+    issue(t0, m0);
+    if (m1.p < 0) break;
+    step(t1, m1);
+    issue(t1, m1);
+    if (m2.p < 0) break;
+    step(t2, m2);
   }
 }
 
@@ -864,21 +897,17 @@ __global__ __launch_bounds__(64) void attn_stream_merge_kernel(AttnParams prm) {
     return;
   }
   const int nsub = prm.seq_prefix[prm.num_seqs];
-  const long long total = (long long)prm.num_kv_heads * nsub;
-  const long long chunk = stream_chunk(total, prm.stream_wgs * kWaves);
-  const long long A = (long long)h * nsub + prm.seq_prefix[s];
-  const long long E = A + (ctx + kSub - 1) / kSub;
-  const long long j1 = A / chunk, j2 = (E - 1) / chunk;
-  if (j1 == j2) return;  // one wave covered it and wrote `out`
-  const int npieces = (int)(j2 - j1 + 1);
-  // piece k: wave j1 + k; the first one sits in slot 1 unless it starts its chunk
-  auto slot_of = [&](int k) -> size_t {
-    const long long j = j1 + k;
-    return (size_t)j * 2 + ((k == 0 && A != j1 * chunk) ? 1 : 0);
-  };
+  const int chunk = stream_chunk(prm.num_kv_heads * nsub, prm.stream_wgs * kWaves);
+  const int A = h * nsub + prm.seq_prefix[s];
+  const int E = A + (ctx + kSub - 1) / kSub;
+  const int k1 = A / chunk, k2 = (E - 1) / chunk;
+  if (k1 == k2) return;  // one wave covered it and wrote `out`
+  // wave k's piece sits in its slot 0 unless the sequence starts inside chunk k1
+  const int first_slot = k1 * 2 + (A != k1 * chunk ? 1 : 0);
+  auto row_of = [&](int k) -> size_t { return (size_t)(k == k1 ? first_slot : k * 2) * G + g; };
 
   float M = kNegInf;
-  for (int k = lane; k < npieces; k += 64) M = fmaxf(M, prm.part_ml[(slot_of(k) * G + g) * 2]);
+  for (int k = k1 + lane; k <= k2; k += 64) M = fmaxf(M, prm.part_ml[row_of(k) * 2]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
@@ -886,13 +915,14 @@ __global__ __launch_bounds__(64) void attn_stream_merge_kernel(AttnParams prm) {
 #pragma unroll
   for (int j = 0; j < kPer; ++j) o[j] = 0.f;
   float lsum = 0.f;
-  for (int k = 0; k < npieces; ++k) {
-    const size_t sl = slot_of(k) * G + g;
-    const float2 ml = *reinterpret_cast<const float2*>(prm.part_ml + sl * 2);
+#pragma unroll 4
+  for (int k = k1; k <= k2; ++k) {
+    const size_t row = row_of(k);
+    const float2 ml = *reinterpret_cast<const float2*>(prm.part_ml + row * 2);
     const float f = ml.x == kNegInf ? 0.f : fast_exp2(ml.x - M);
     lsum += f * ml.y;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) o[j] += f * prm.part_o[sl * D + lane + 64 * j];
+    for (int j = 0; j < kPer; ++j) o[j] += f * prm.part_o[row * D + lane + 64 * j];
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll

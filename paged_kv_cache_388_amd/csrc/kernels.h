@@ -22,6 +22,10 @@ constexpr int kSubTokens = 16;
 constexpr int kStreamWaves = 4;           // waves per workgroup
 constexpr int kMaxStreamSeqs = 4096;      // batch limit (per-sequence tables live in LDS)
 constexpr int kMinChunk = 4;              // sub-tiles per wave at least
+// Positions (H_kv x sub-tiles of the batch) the stream path indexes in 32 bits;
+// the host sends calls whose bound B * ceil(max_ctx / 16) * H_kv exceeds it to
+// the grid path.
+constexpr int kMaxStreamPositions = 1 << 28;
 
 // ---- grid path (batches above kMaxStreamSeqs) --------------------------------
 // One workgroup per (kv head, sequence, partition of kPartitionTokens tokens).
@@ -42,13 +46,13 @@ struct AttnParams {
   int32_t num_blocks;
   int32_t max_context_len;
   float scale_log2;             // scale * log2(e): logits kept in base-2 units
-  // Workspace views.  Stream path: part_o [2 * waves, G, D], part_ml
-  // [2 * waves, G, 2] (max logit in log2 units, normaliser), seq_prefix
-  // [B + 1] (sub-tiles of the sequences before each one).  Grid path: part_o
-  // [B, H_q, P, D], part_ml [B, H_q, P, 2], seq_prefix unused.
+  // Workspace views.  Stream path: seq_prefix [B + 1] (sub-tiles of the
+  // sequences before each one), part_o [2 * waves, G, D], part_ml
+  // [2 * waves, G, 2] (max logit in log2 units, normaliser).  Grid path:
+  // part_o [B, H_q, P, D], part_ml [B, H_q, P, 2]; seq_prefix unused.
+  int32_t* seq_prefix;
   float* part_o;
   float* part_ml;
-  int32_t* seq_prefix;
   int32_t stream_wgs;           // > 0: stream path with this many workgroups
   int32_t max_partitions;       // grid path: ceil(max_context_len / kPartitionTokens)
 };

@@ -73,10 +73,15 @@ int stream_workgroups() {
   return wgs;
 }
 
-// Workgroups of the stream path for this batch on the current device, or 0
-// for the grid path (batches above kMaxStreamSeqs).
-int32_t stream_wgs_for(int32_t num_seqs) {
-  return num_seqs <= pkv::kMaxStreamSeqs ? stream_workgroups() : 0;
+// Workgroups of the stream path for this call on the current device, or 0
+// for the grid path (batches above kMaxStreamSeqs, or more positions than the
+// stream path indexes).
+int32_t stream_wgs_for(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+  if (num_seqs > pkv::kMaxStreamSeqs) return 0;
+  const long long subs = ((long long)(max_context_len > 0 ? max_context_len : 0) + pkv::kSubTokens - 1) /
+                         pkv::kSubTokens;
+  if ((long long)num_seqs * num_kv_heads * subs > pkv::kMaxStreamPositions) return 0;
+  return stream_workgroups();
 }
 
 int32_t partitions_for(int32_t max_context_len) {
@@ -131,7 +136,7 @@ size_t paged_attention_workspace_bytes(pkv_pool pool, int32_t num_seqs, int32_t 
     return 0;
   g_err[0] = '\0';
   return pkv::attn_workspace_layout(num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim,
-                                    max_context_len, stream_wgs_for(num_seqs))
+                                    max_context_len, stream_wgs_for(num_seqs, pool.num_kv_heads, max_context_len))
       .bytes;
 }
 
@@ -160,7 +165,7 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_cache,
     return fail(PKV_EINVAL, "null pointer argument");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_EINVAL, "out, q and the pools must be 16-byte aligned");
-  const int32_t stream_wgs = stream_wgs_for(num_seqs);
+  const int32_t stream_wgs = stream_wgs_for(num_seqs, pool.num_kv_heads, max_context_len);
   const pkv::AttnWorkspace lay = pkv::attn_workspace_layout(
       num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim, max_context_len, stream_wgs);
   if (lay.bytes > 0 && (!workspace || workspace_bytes < lay.bytes))
