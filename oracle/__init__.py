@@ -21,6 +21,7 @@ from .paged_attention import (  # noqa: F401
     last_block_fill,
     mean_tail_waste,
     merge_partitions,
+    multi_query_attention,
     partition_states,
     split_decode_attention,
     storage_to_f64,

@@ -171,6 +171,63 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale,
 
 
 # ---------------------------------------------------------------------------
+# several new tokens per sequence: speculative-decode verification and
+# chunked-prefill chunks
+# ---------------------------------------------------------------------------
+
+def multi_query_attention(q, k_cache, v_cache, block_tables, context_lens, query_lens,
+                          scale, dtype):
+    """Paged attention of several new tokens per sequence, in fp64.
+
+    A chunk of a long prompt is processed together with other requests' decode
+    tokens (the second page, "Chunked Prefill"), and a large model checks a
+    draft model's guessed tokens in one pass (*The Memory Wall*, "The Next
+    Frontier: Speculative Decoding and Beyond").  Both put L_s new tokens of
+    sequence s through attention at once.  Reading taken: the L_s new tokens
+    are the last L_s of the sequence's n_s cached tokens (their K/V were
+    appended first), and new token i, at logical position n_s - L_s + i,
+    attends to logical tokens 0 .. n_s - L_s + i (itself and everything
+    before it).  L_s = 1 is decode.
+
+    q            [T, H_q, D]   the new tokens, packed sequence by sequence
+                               (T = sum of query_lens, no padding)
+    k_cache      [NB, H_kv, bs, D]
+    v_cache      [NB, H_kv, bs, D]
+    block_tables [B, max_blocks]
+    context_lens [B]           n_s, counting the new tokens
+    query_lens   [B]           L_s, 0 <= L_s <= n_s
+    Returns fp64 ``[T, H_q, D]``.
+    """
+    T, H_q, D = q.shape
+    H_kv = k_cache.shape[1]
+    if H_q % H_kv != 0:
+        raise ValueError("H_q must be a multiple of H_kv")
+    G = H_q // H_kv
+    query_lens = [int(x) for x in query_lens]
+    if sum(query_lens) != T:
+        raise ValueError("query_lens must sum to the number of query rows")
+    out = np.zeros((T, H_q, D))
+    row = 0
+    for s, L in enumerate(query_lens):
+        n = int(context_lens[s])
+        if L > n:
+            raise ValueError("a sequence has more new tokens than cached tokens")
+        if L == 0:
+            continue
+        K = gather_context(k_cache, block_tables[s], n, dtype)
+        V = gather_context(v_cache, block_tables[s], n, dtype)
+        for i in range(L):
+            visible = n - L + i + 1
+            qs = storage_to_f64(q[row + i], dtype)
+            for h in range(H_q):
+                kv = h // G
+                scores = scale * (K[kv, :visible] @ qs[h])
+                out[row + i, h] = _softmax_weighted_sum(scores, V[kv, :visible])
+        row += L
+    return out
+
+
+# ---------------------------------------------------------------------------
 # split-context decode: per-partition softmax state and its exact merge
 # ---------------------------------------------------------------------------
 
