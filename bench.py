@@ -39,12 +39,26 @@ METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) and seqs/s"
 
 
 def algorithmic_bytes(w):
-    """Bytes paged_attention_decode must move for one call: every context
-    token's K and V once, q in, out back, the block ids and context lengths."""
+    """Bytes one attention call must move: every context token's K and V once,
+    q in and out back (one row per new token), the block ids, the context
+    lengths (and the query-row prefix of a multi-token call)."""
     b = wl.ELEM_BYTES[w.dtype]
     ids = sum((int(n) + w.block_size - 1) // w.block_size for n in w.context_lens)
-    return (w.kv_bytes() + 2 * w.num_seqs * w.num_q_heads * w.head_dim * b + 4 * ids
-            + 4 * w.num_seqs)
+    rows = w.q.shape[0]
+    extra = 4 * (w.num_seqs + 1) if w.multi else 0
+    return (w.kv_bytes() + 2 * rows * w.num_q_heads * w.head_dim * b + 4 * ids
+            + 4 * w.num_seqs + extra)
+
+
+def attention_flops(w):
+    """QK and PV multiply-adds of one call: 4 * D flops per (new token, query
+    head, visible context token)."""
+    G = w.num_q_heads // w.num_kv_heads
+    qlens = np.diff(w.query_start) if w.multi else (w.context_lens > 0).astype(np.int64)
+    visible = 0
+    for n, L in zip(w.context_lens.astype(np.int64), qlens):
+        visible += int(L) * int(n) - int(L) * (int(L) - 1) // 2
+    return 4 * w.head_dim * G * w.num_kv_heads * visible
 
 
 def counter_traffic(workload):
@@ -89,8 +103,14 @@ def cpu_baseline(w, min_seconds):
         kv = 0
         while True:
             for s in range(w.num_seqs):
-                oracle.decode_attention(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
-                                        w.dtype, seq_ids=[s])
+                if w.multi:
+                    r0, r1 = int(w.query_start[s]), int(w.query_start[s + 1])
+                    oracle.multi_query_attention(w.q[r0:r1], kc, vc, w.block_tables[s:s + 1],
+                                                 w.context_lens[s:s + 1], [r1 - r0], w.scale,
+                                                 w.dtype)
+                else:
+                    oracle.decode_attention(w.q, kc, vc, w.block_tables, w.context_lens,
+                                            w.scale, w.dtype, seq_ids=[s])
                 seqs += 1
                 kv += 2 * int(w.context_lens[s]) * w.num_kv_heads * w.head_dim * b
                 if time.perf_counter() - t1 > min_seconds:
@@ -166,7 +186,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b_gqa",
-                    help="one of: " + ", ".join(wl.NAMED[:4]) + ", long_ctx_bs16, long_ctx_bs32")
+                    help="one of: " + ", ".join(wl.NAMED[:4]) + ", long_ctx_bs16, long_ctx_bs32, "
+                         + ", ".join(wl.MULTI))
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="duration of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--read-probe-mib", type=int, default=0,
@@ -219,8 +240,13 @@ def main():
     slot_mapping = up(w.slot_mapping.astype(np.int32))
     new_key, new_value = up(w.new_key), up(w.new_value)
     out = torch.empty_like(q)
-    ws_bytes = _lib.paged_attention_workspace_bytes(k_cache, w.num_seqs, w.num_q_heads,
-                                                    w.max_context_len)
+    if w.multi:
+        query_start = up(w.query_start.astype(np.int32))
+        ws_bytes = _lib.paged_attention_multi_workspace_bytes(k_cache, w.num_seqs, w.num_q_heads,
+                                                              w.max_query_len, w.max_context_len)
+    else:
+        ws_bytes = _lib.paged_attention_workspace_bytes(k_cache, w.num_seqs, w.num_q_heads,
+                                                        w.max_context_len)
     workspace = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     max_ctx = w.max_context_len
     torch.cuda.synchronize()
@@ -232,8 +258,12 @@ def main():
             _lib.paged_kv_append(new_key, new_value, k_cache, v_cache, slot_mapping)
 
     def attend():
-        _lib.paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
-                                    w.scale, max_ctx, workspace)
+        if w.multi:
+            _lib.paged_attention_multi(out, q, k_cache, v_cache, block_tables, context_lens,
+                                       query_start, w.scale, max_ctx, w.max_query_len, workspace)
+        else:
+            _lib.paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
+                                        w.scale, max_ctx, workspace)
 
     for _ in range(args.warmup):
         write_step()
@@ -278,10 +308,14 @@ def main():
                    "block_size": w.block_size, "num_blocks": w.num_blocks,
                    "mean_context": round(float(w.context_lens.mean()), 1),
                    "max_context": max_ctx, "kv_bytes_per_step": kv, "seed": w.seed,
-                   "step": "copy_blocks + paged_kv_append + paged_attention_decode",
+                   "step": ("copy_blocks + paged_kv_append + "
+                            + ("paged_attention_multi" if w.multi else "paged_attention_decode")),
+                   "new_tokens": int(w.q.shape[0]),
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "seqs_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
+        "new_tokens_per_s": round(w.q.shape[0] / (ms_per_step * 1e-3), 1),
+        "attention_tflops": round(attention_flops(w) / (attn_avg_ms * 1e-3) / 1e12, 2),
         "attention_ms": {"mean": round(attn_avg_ms, 4),
                          "p10": round(float(np.percentile(attn_ms, 10)), 4),
                          "p50": round(float(np.percentile(attn_ms, 50)), 4),
@@ -290,7 +324,9 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": counter_traffic(w.name),
                      "kernel": (f"attn_stream_kernel<{w.dtype},{w.head_dim},{w.block_size}> + "
-                                "attn_stream_merge_kernel (one paged_attention_decode call)"),
+                                "attn_stream_merge_kernel (one "
+                                f"{'paged_attention_multi' if w.multi else 'paged_attention_decode'}"
+                                " call)"),
                      "algorithmic_bytes_per_launch": alg},
         "cpu_baseline": cpu,
     }

@@ -152,6 +152,60 @@ PKV_API pkv_status paged_attention_decode(void* out, const void* q,
                                           hipStream_t stream);
 
 /*
+ * Bytes of workspace paged_attention_multi needs for this shape on the
+ * current device, or 0 for invalid input or a call it refuses (more than 2048
+ * sequences, or more than 2^28 positions: kv heads x 16-column groups x
+ * 16-token sub-tiles).
+ */
+PKV_API size_t paged_attention_multi_workspace_bytes(pkv_pool pool, int32_t num_seqs,
+                                                     int32_t num_q_heads, int32_t max_query_len,
+                                                     int32_t max_context_len);
+
+/*
+ * paged_attention_multi — several new tokens per sequence attend to the
+ * paged context at once: a chunk of a long prompt batched with other
+ * requests' decode tokens (the second page, "Chunked Prefill: Don't Let Long
+ * Prompts Consume the Entire Budget"), or a large model verifying a draft
+ * model's guessed tokens in one pass ("The Memory Wall", "The Next Frontier:
+ * Speculative Decoding and Beyond").  Sequence s has n = context_lens[s]
+ * cached tokens whose last L = query_start[s+1] - query_start[s] are its new
+ * ones (their K/V already appended); new token i (0 <= i < L), query row
+ * query_start[s] + i, attends to logical tokens 0 .. n - L + i:
+ *
+ *     out[row, h, :] = softmax_t(scale * q[row, h, :] . K_s[h/G, t, :]) @ V_s[h/G, t, :],
+ *                      t <= n - L + i
+ *
+ * With L = 1 for every sequence this is paged_attention_decode.  The kernel's
+ * MFMA columns are (new token, query head) pairs in groups of 16; each group
+ * streams the sequence's context once, so L * G <= 16 (e.g. 4 draft tokens
+ * at G = 4) reads every K/V byte once, and longer chunks re-read it once per
+ * further group.  Precision, determinism and metadata trust as for
+ * paged_attention_decode; rows of a sequence are clamped to
+ * [0, num_query_tokens] and to at most min(n, max_query_len), so malformed
+ * query_start values never move a read or write outside its buffer.
+ *
+ *   out, q        [num_query_tokens, num_q_heads, head_dim]  pool dtype, rows
+ *                 packed sequence by sequence (no padding)
+ *   query_start   [num_seqs + 1] int32 device prefix of query rows,
+ *                 query_start[0] = 0, non-decreasing, last = num_query_tokens
+ *   max_query_len host-known upper bound of L over the batch
+ *   other arguments as for paged_attention_decode; num_seqs <= 2048
+ *   workspace     >= paged_attention_multi_workspace_bytes(...) bytes
+ */
+PKV_API pkv_status paged_attention_multi(void* out, const void* q,
+                                         const void* k_cache, const void* v_cache,
+                                         pkv_pool pool,
+                                         const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens,
+                                         const int32_t* query_start,
+                                         int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t num_query_tokens, int32_t max_query_len,
+                                         float scale, int32_t max_context_len,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/*
  * paged_copy_blocks — copy-on-write block duplication ("05 PagedAttention",
  * "KV Cache Sharing (Copy-on-Write)": a sequence that diverges gets its own
  * copy of a shared block while the shared block stays as it was).  For each

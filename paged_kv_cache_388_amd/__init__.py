@@ -9,6 +9,8 @@ Importing the package loads nothing; the library is loaded on first use.
 from ._lib import (  # noqa: F401
     PagedKVError,
     paged_attention_decode,
+    paged_attention_multi,
+    paged_attention_multi_workspace_bytes,
     paged_attention_workspace_bytes,
     paged_copy_blocks,
     paged_kv_append,

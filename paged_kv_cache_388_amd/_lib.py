@@ -53,6 +53,11 @@ def load():
     lib.paged_attention_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, PkvPool, c_vp, c_i32, c_vp,
                                            c_i32, c_i32, c_f, c_i32, c_vp, c_sz, c_vp]
     lib.paged_attention_decode.restype = c_i32
+    lib.paged_attention_multi_workspace_bytes.argtypes = [PkvPool, c_i32, c_i32, c_i32, c_i32]
+    lib.paged_attention_multi_workspace_bytes.restype = c_sz
+    lib.paged_attention_multi.argtypes = [c_vp, c_vp, c_vp, c_vp, PkvPool, c_vp, c_i32, c_vp, c_vp,
+                                          c_i32, c_i32, c_i32, c_i32, c_f, c_i32, c_vp, c_sz, c_vp]
+    lib.paged_attention_multi.restype = c_i32
     lib.paged_copy_blocks.argtypes = [c_vp, c_vp, PkvPool, c_vp, c_i32, c_vp]
     lib.paged_copy_blocks.restype = c_i32
     lib.pkv_stream_copy.argtypes = [c_vp, c_vp, c_sz, c_vp]
@@ -165,6 +170,46 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), pool, _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), B, Hq, float(scale), int(max_context_len),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def paged_attention_multi_workspace_bytes(k_cache, num_seqs, num_q_heads, max_query_len,
+                                          max_context_len):
+    """Workspace bytes paged_attention_multi needs on the current device (0 if
+    the call would be refused)."""
+    return int(load().paged_attention_multi_workspace_bytes(
+        pool_of(k_cache), int(num_seqs), int(num_q_heads), int(max_query_len),
+        int(max_context_len)))
+
+
+def paged_attention_multi(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                          scale, max_context_len, max_query_len, workspace=None, stream=None):
+    """Several new tokens per sequence: q/out [T, H_q, D] packed by sequence,
+    query_start [B + 1] int32 (rows of sequence s are query_start[s] ..
+    query_start[s+1] - 1; they are the last tokens of its context_lens[s])."""
+    pool = _pools(k_cache, v_cache)
+    dev = k_cache.device
+    _need(q, "q", dtype=k_cache.dtype, dim=3, device=dev)
+    _need(out, "out", dtype=k_cache.dtype, dim=3, device=dev)
+    if out.shape != q.shape or q.shape[2] != k_cache.shape[3]:
+        raise ValueError("q/out must be [T, H_q, D] with the pool's D")
+    _need(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _need(context_lens, "context_lens", dtype=torch.int32, dim=1, device=dev)
+    _need(query_start, "query_start", dtype=torch.int32, dim=1, device=dev)
+    B = context_lens.shape[0]
+    T, Hq, _ = q.shape
+    if block_tables.shape[0] != B or query_start.shape[0] != B + 1:
+        raise ValueError("block_tables [B, *], context_lens [B], query_start [B + 1] disagree")
+    need = paged_attention_multi_workspace_bytes(k_cache, B, Hq, max_query_len, max_context_len)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", device=dev)
+    _check(load().paged_attention_multi(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), pool, _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), _ptr(query_start), B, Hq, T,
+        int(max_query_len), float(scale), int(max_context_len), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

@@ -631,30 +631,71 @@ __global__ __launch_bounds__(64) void attn_reduce_kernel(AttnParams prm) {
 // ===========================================================================
 // Stream path
 // ===========================================================================
+//
+// Columns.  A sequence's MFMA columns are (new token i, query head g) pairs,
+// c = i * G + g, cut into groups of 16.  Decode has one new token, so one
+// group of G columns.  With L new tokens a sequence has ceil(L * G / 16)
+// groups; each group streams the sequence's whole context once.  Column c
+// sees logical tokens 0 .. n - L + i (itself and everything before it).
 
-// Where a global position lies: kv head h, sequence s, and the global
-// positions [A, E) of that (head, sequence)'s sub-tiles.  sS is the LDS prefix
-// of sub-tile counts (sS[s] = sub-tiles of sequences 0..s-1, sS[B] = nsub),
-// so sequence s owns [h*nsub + sS[s], h*nsub + sS[s+1]).  Wave-uniform.
+// Per-sequence column geometry, all wave-uniform.
+struct SeqCols {
+  int n;      // cached tokens
+  int L;      // new tokens (query rows)
+  int q0;     // first query row
+  int ngrp;   // column groups
+};
+
+template <bool MULTI>
+__device__ __forceinline__ SeqCols seq_cols(const int* sCtx, const int* sQS, const int* sQL, int s,
+                                            int G) {
+  SeqCols c;
+  c.n = uniform(sCtx[s]);
+  if constexpr (MULTI) {
+    c.q0 = uniform(sQS[s]);
+    c.L = uniform(sQL[s]);
+    c.ngrp = (c.L * G + kSub - 1) / kSub;
+  } else {
+    c.q0 = s;
+    c.L = c.n > 0 ? 1 : 0;
+    c.ngrp = c.L;
+  }
+  return c;
+}
+
+// Where a global position lies: kv head h, sequence s, column group cg, and
+// the global positions [A, E) of that (head, sequence, group)'s sub-tiles.
+// sS is the LDS prefix of positions per kv head (sS[s] = positions of
+// sequences 0..s-1, sS[B] = per-head total); sequence s owns
+// [h*per + sS[s], h*per + sS[s+1]), group after group.  Wave-uniform.
 struct SeqSpan {
-  int h, s;
+  int h, s, cg;
   int A, E;
 };
 
-__device__ __forceinline__ SeqSpan locate(int p, int nsub, const int* sS, int B) {
+template <bool MULTI>
+__device__ __forceinline__ SeqSpan locate(int p, int per, const int* sS, const int* sCtx, int B) {
   SeqSpan sp;
-  sp.h = p / nsub;
-  const int rr = p - sp.h * nsub;
-  // largest s with sS[s] <= rr: skips empty sequences, which own no position
+  sp.h = p / per;
+  const int rr = p - sp.h * per;
+  // largest s with sS[s] <= rr: skips sequences that own no position
   int a = 0, b = B - 1;
   while (a < b) {
     const int mid = (a + b + 1) >> 1;
     if (uniform(sS[mid]) <= rr) a = mid; else b = mid - 1;
   }
   sp.s = a;
-  const int base = sp.h * nsub;
-  sp.A = base + uniform(sS[a]);
-  sp.E = base + uniform(sS[a + 1]);
+  const int base = sp.h * per + uniform(sS[a]);
+  if constexpr (MULTI) {
+    const int nsub = (uniform(sCtx[a]) + kSub - 1) / kSub;
+    sp.cg = (rr - uniform(sS[a])) / nsub;
+    sp.A = base + sp.cg * nsub;
+    sp.E = sp.A + nsub;
+  } else {
+    sp.cg = 0;
+    sp.A = base;
+    sp.E = sp.h * per + uniform(sS[a + 1]);
+  }
   return sp;
 }
 
@@ -662,7 +703,7 @@ __device__ __forceinline__ SeqSpan locate(int p, int nsub, const int* sS, int B)
 // [v * chunk, min((v + 1) * chunk, total)).  The cut depends only on total
 // and the grid, so every piece boundary, and with it the result, is fixed by
 // the context lengths.  total <= kMaxStreamPositions (the host routes larger
-// calls to the grid path).
+// calls elsewhere).
 __device__ __forceinline__ int stream_chunk(int total, int waves) {
   const int c = total / waves + (total % waves != 0);
   return c < kMinChunk ? kMinChunk : c;
@@ -682,14 +723,45 @@ __device__ __forceinline__ int load_id_batch(const AttnParams& prm, int s, int b
   return j < nblk ? prm.block_tables[(size_t)s * prm.max_blocks_per_seq + j] : -1;
 }
 
-template <int DT, int D, int BS>
+// Query operand of column group cg (B of the QK MFMA): lane (r, col) holds
+// column c = 16*cg + col, i.e. new token c / G of the sequence and query head
+// h*G + c % G, 16-byte chunks r + 4*kk of that row; zero for columns past
+// the sequence's L*G.
+template <int N, bool MULTI>
+__device__ __forceinline__ void load_query_cols(uint4 (&qb)[N], const void* q, const SeqCols& sc,
+                                                int h, int cg, int G, int Hq, int lane) {
+  constexpr int kRow = 64 * N;
+  const int r = lane >> 4;
+  const int c = cg * kSub + (lane & 15);
+  const bool ok = c < sc.L * G;
+  const int i = ok ? (MULTI ? c / G : 0) : 0, g = ok ? (MULTI ? c % G : c) : 0;
+  const char* qrow = static_cast<const char*>(q) +
+                     ((size_t)(sc.q0 + i) * Hq + (size_t)h * G + g) * kRow;
+#pragma unroll
+  for (int kk = 0; kk < N; ++kk)
+    qb[kk] = ok ? *reinterpret_cast<const uint4*>(qrow + 16 * (r + 4 * kk)) : make_uint4(0, 0, 0, 0);
+}
+
+// Tokens of sub-tile t that column group cg can see at all (its last
+// column's causal limit), 0..16: later rows are not loaded.
+__device__ __forceinline__ int group_rows(const SeqCols& sc, int cg, int G, int t) {
+  int i_last = (cg * kSub + kSub - 1) / G;
+  i_last = i_last < sc.L - 1 ? i_last : sc.L - 1;
+  int v = sc.n - sc.L + i_last + 1 - t * kSub;
+  return v > kSub ? kSub : v;
+}
+
+template <int DT, int D, int BS, bool MULTI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_stream_kernel(AttnParams prm) {
   using Geo = Geometry<DT, D, BS>;
   constexpr int N = Geo::N;
   constexpr int kMM = Geo::kMM;
-  __shared__ int sS[kMaxStreamSeqs + 1];
-  __shared__ int sCtx[kMaxStreamSeqs];
+  constexpr int kMaxSeqs = MULTI ? kMaxMultiSeqs : kMaxStreamSeqs;
+  __shared__ int sS[kMaxSeqs + 1];
+  __shared__ int sCtx[kMaxSeqs];
+  __shared__ int sQS[MULTI ? kMaxSeqs : 1];  // first query row
+  __shared__ int sQL[MULTI ? kMaxSeqs : 1];  // query rows
   __shared__ int sScan[kWaves];
   __shared__ __attribute__((aligned(16))) char sK[kWaves][kSub * Geo::kRow];
 
@@ -701,16 +773,32 @@ void attn_stream_kernel(AttnParams prm) {
   const int G = prm.group;
   const int Hq = prm.num_q_heads;
 
-  // ---- sub-tile prefix over the batch (every workgroup, in LDS) -------------
-  const int per = (B + kThreads - 1) / kThreads;
+  // ---- per-sequence tables and the position prefix (every workgroup, LDS) ---
+  // Multi-token: query rows [query_start[s], query_start[s+1]) clamped to
+  // [0, num_query_tokens], and at most min(n, max_query_len) of them, so that
+  // no index derived from them leaves its buffer whatever the metadata holds.
+  const int per_thread = (B + kThreads - 1) / kThreads;
   int mine = 0;
-  for (int k = 0; k < per; ++k) {
-    const int s = tid * per + k;
+  for (int k = 0; k < per_thread; ++k) {
+    const int s = tid * per_thread + k;
     if (s < B) {
       int c = prm.context_lens[s];
       c = c < 0 ? 0 : (c > prm.max_context_len ? prm.max_context_len : c);
+      int groups = c > 0 ? 1 : 0;
+      if constexpr (MULTI) {
+        const int T = prm.num_query_tokens;
+        int q0 = prm.query_start[s], qe = prm.query_start[s + 1];
+        q0 = q0 < 0 ? 0 : (q0 > T ? T : q0);
+        qe = qe < q0 ? q0 : (qe > T ? T : qe);
+        int L = qe - q0;
+        L = L < c ? L : c;
+        L = L < prm.max_query_len ? L : prm.max_query_len;
+        sQS[s] = q0;
+        sQL[s] = L;
+        groups = (L * G + kSub - 1) / kSub;
+      }
       sCtx[s] = c;
-      mine += (c + kSub - 1) / kSub;
+      mine += groups * ((c + kSub - 1) / kSub);
     }
   }
   int incl = mine;
@@ -723,11 +811,13 @@ void attn_stream_kernel(AttnParams prm) {
   __syncthreads();
   int run = incl - mine;
   for (int ww = 0; ww < w; ++ww) run += sScan[ww];
-  for (int k = 0; k < per; ++k) {
-    const int s = tid * per + k;
+  for (int k = 0; k < per_thread; ++k) {
+    const int s = tid * per_thread + k;
     if (s < B) {
       sS[s] = run;
-      run += (sCtx[s] + kSub - 1) / kSub;
+      int groups = sCtx[s] > 0 ? 1 : 0;
+      if constexpr (MULTI) groups = (sQL[s] * G + kSub - 1) / kSub;
+      run += groups * ((sCtx[s] + kSub - 1) / kSub);
     }
   }
   if (tid == 0) sS[B] = sScan[0] + sScan[1] + sScan[2] + sScan[3];
@@ -736,8 +826,8 @@ void attn_stream_kernel(AttnParams prm) {
     for (int s = tid; s <= B; s += kThreads) prm.seq_prefix[s] = sS[s];
 
   // ---- this wave's chunk of positions -----------------------------------------
-  const int nsub = uniform(sS[B]);
-  const int total = prm.num_kv_heads * nsub;
+  const int per = uniform(sS[B]);  // positions per kv head
+  const int total = prm.num_kv_heads * per;
   const int chunk = stream_chunk(total, (int)gridDim.x * kWaves);
   const int wv = xcd_remap(blockIdx.x, gridDim.x) * kWaves + w;
   const int a = (int)min((long long)wv * chunk, (long long)total);
@@ -752,19 +842,20 @@ void attn_stream_kernel(AttnParams prm) {
   // ---- issue cursor: next position whose tiles are loaded ---------------------
   int pi = a;
   SeqSpan si;
-  int ctx_i = 0, nblk_i = 0, blk0_i = 0, ids_i = -1;
+  SeqCols ci;
+  int nblk_i = 0, blk0_i = 0, ids_i = -1;
   // Block ids arrive in 64-entry batches.  The wait for a batch is taken
-  // where it is loaded (a sequence entry, or every 64 blocks): loads issued
-  // on some paths only would otherwise make the wait at every lookup drain
-  // the tiles in flight.
+  // where it is loaded (a group entry, or every 64 blocks): loads issued on
+  // some paths only would otherwise make the wait at every lookup drain the
+  // tiles in flight.
   auto load_ids_now = [&]() {
     ids_i = load_id_batch(prm, si.s, blk0_i, nblk_i, lane);
     asm volatile("" : "+v"(ids_i));
   };
   auto enter_issue_seq = [&]() {
-    si = locate(pi, nsub, sS, B);
-    ctx_i = uniform(sCtx[si.s]);
-    nblk_i = (ctx_i + BS - 1) / BS;
+    si = locate<MULTI>(pi, per, sS, sCtx, B);
+    ci = seq_cols<MULTI>(sCtx, sQS, sQL, si.s, G);
+    nblk_i = (ci.n + BS - 1) / BS;
     blk0_i = (pi - si.A) * kSub / BS;
     load_ids_now();
   };
@@ -782,13 +873,19 @@ void attn_stream_kernel(AttnParams prm) {
       int phys = __builtin_amdgcn_readlane(ids_i, blk - blk0_i);
       const bool ok = (unsigned)phys < (unsigned)prm.num_blocks;
       phys = ok ? phys : 0;
-      int valid = ctx_i - tsub * kSub;
-      valid = valid > kSub ? kSub : valid;
+      int rows;
+      if constexpr (MULTI) {
+        rows = group_rows(ci, uniform(si.cg), G, tsub);
+      } else {
+        rows = ci.n - tsub * kSub;
+        rows = rows > kSub ? kSub : rows;
+      }
       const size_t sub = ((size_t)phys * prm.num_kv_heads + uniform(si.h)) * Geo::kTileBytes +
                          (tsub * kSub % BS) * Geo::kRow;
-      // the range ends at the last real token: later rows, and every row of a
-      // block id outside the pool, read as zeros without touching memory
-      const int nrec = uniform(ok ? valid * Geo::kRow : 0);
+      // the range ends at the last row any column can see: later rows, and
+      // every row of a block id outside the pool, read as zeros without
+      // touching memory
+      const int nrec = uniform(ok && rows > 0 ? rows * Geo::kRow : 0);
       load_tile<N>(t, make_rsrc(static_cast<const char*>(prm.k_cache) + sub, nrec),
                    make_rsrc(static_cast<const char*>(prm.v_cache) + sub, nrec), koff, voff);
       ++pi;
@@ -801,41 +898,46 @@ void attn_stream_kernel(AttnParams prm) {
   };
 
   // ---- compute cursor -----------------------------------------------------------
-  // The open piece: positions [p0, ...) of sequence span sc.  A piece that
-  // does not cover its whole sequence sits in partial slot 0 of this wave if
-  // it starts the chunk, else in slot 1 (only the chunk's last piece can).
+  // The open piece: positions [p0, ...) of group span sc.  A piece that does
+  // not cover its whole group sits in partial slot 0 of this wave if it
+  // starts the chunk, else in slot 1 (only the chunk's last piece can).
+  const int cols = prm.slot_cols;
   bool open = false;
   int p0 = 0;
   SeqSpan sc;
-  int ctx_c = 0;
+  SeqCols cc;
+  int vis_c = 0;  // this lane's column: tokens it can see (0 for a padding column)
   uint4 qb[N];
   WaveState<kMM> st;
   auto finish_piece = [&](int p_end) {
     float l = st.l + __shfl_xor(st.l, 16);
     l += __shfl_xor(l, 32);
-    const int g = lane & 15;
-    if (g < G) {
-      float o[D / 4];
-      lane_run<D, kMM>(o, st);
-      const size_t row = (size_t)sc.s * Hq + (size_t)sc.h * G + g;
-      if (p0 == sc.A && p_end == sc.E) {
+    const int col = lane & 15;
+    const int c = sc.cg * kSub + col;
+    float o[D / 4];
+    lane_run<D, kMM>(o, st);
+    if (p0 == sc.A && p_end == sc.E) {
+      if (c < cc.L * G) {
+        const size_t row = MULTI ? (size_t)(cc.q0 + c / G) * Hq + (size_t)sc.h * G + c % G
+                                 : (size_t)cc.q0 * Hq + (size_t)sc.h * G + c;
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
         for (int i = 0; i < D / 4; ++i) o[i] *= inv;
         store_run<DT, D>(static_cast<char*>(prm.out) + (row * D + r * (D / 4)) * Geo::EB, o);
-      } else {
-        const size_t slot = (size_t)wv * 2 + (p0 == a ? 0 : 1);
-        store_run<DT_F32, D>(prm.part_o + (slot * G + g) * D + r * (D / 4), o);
-        if (r == 0) *reinterpret_cast<float2*>(prm.part_ml + (slot * G + g) * 2) = make_float2(st.m, l);
       }
+    } else if (col < cols) {
+      const size_t slot = (size_t)wv * 2 + (p0 == a ? 0 : 1);
+      store_run<DT_F32, D>(prm.part_o + (slot * cols + col) * D + r * (D / 4), o);
+      if (r == 0)
+        *reinterpret_cast<float2*>(prm.part_ml + (slot * cols + col) * 2) = make_float2(st.m, l);
     }
   };
   auto step = [&](Tile<N>& t, const SlotMeta& m) {
     if (!open) {
-      sc = locate(m.p, nsub, sS, B);
-      ctx_c = uniform(sCtx[sc.s]);
+      sc = locate<MULTI>(m.p, per, sS, sCtx, B);
+      cc = seq_cols<MULTI>(sCtx, sQS, sQL, sc.s, G);
       p0 = m.p;
-      load_query<N>(qb, prm.q, sc.s, sc.h, G, Hq, lane);
+      load_query_cols<N, MULTI>(qb, prm.q, cc, sc.h, sc.cg, G, Hq, lane);
       // Take the wait for the query here, where a piece opens: the loads are
       // conditional, and a wait placed at their use would drain every
       // sub-tile's prefetched loads on every step.
@@ -845,11 +947,18 @@ void attn_stream_kernel(AttnParams prm) {
         asm volatile("" : "+v"(qv));
         qb[kk] = __builtin_bit_cast(uint4, qv);
       }
+      if constexpr (MULTI) {
+        const int c = sc.cg * kSub + (lane & 15);
+        vis_c = c < cc.L * G ? cc.n - cc.L + c / G + 1 : 0;
+      }
       st.reset();
       open = true;
     }
     const int tsub = m.p - sc.A;
-    int valid = ctx_c - tsub * kSub;
+    // real tokens of the sub-tile for this lane's column: in decode every
+    // column sees the whole context (padding columns have q = 0 and are
+    // never written), so the count is wave-uniform
+    int valid = (MULTI ? vis_c : cc.n) - tsub * kSub;
     valid = valid > kSub ? kSub : valid;
     attend_subtile<DT, N, kMM>(t, qb, valid, scale_log2, r, st, kst);
     if (m.p + 1 == sc.E || m.p + 1 == b) {
@@ -876,35 +985,56 @@ void attn_stream_kernel(AttnParams prm) {
   }
 }
 
-// Merge of the pieces of one split (sequence, query head): one wave, lanes
-// over the head dim, pieces visited in logical order.  Also writes the zero
-// row of an empty context.
-template <int DT, int D>
+// Merge of the pieces of one split (sequence, kv head, column group) for one
+// column: one wave, lanes over the head dim, pieces visited in logical order.
+// Grid: sequence x kv head x group (up to the call's maximum) x column.  In
+// decode it also writes the zero row of an empty context.
+template <int DT, int D, bool MULTI>
 __global__ __launch_bounds__(64) void attn_stream_merge_kernel(AttnParams prm) {
   const int lane = threadIdx.x;
   const int Hq = prm.num_q_heads;
   const int G = prm.group;
-  const int s = blockIdx.x / Hq;
-  const int hq = blockIdx.x % Hq;
-  const int h = hq / G, g = hq % G;
+  const int cols = prm.slot_cols;
+  const int ngmax = prm.max_groups;
+  int id = blockIdx.x;
+  const int col = id % cols;
+  id /= cols;
+  const int cg = id % ngmax;
+  id /= ngmax;
+  const int h = id % prm.num_kv_heads;
+  const int s = id / prm.num_kv_heads;
   constexpr int kPer = D / 64;
-  const size_t orow = ((size_t)s * Hq + hq) * D;
   int ctx = prm.context_lens[s];
   ctx = ctx < 0 ? 0 : (ctx > prm.max_context_len ? prm.max_context_len : ctx);
-  if (ctx == 0) {
+  int q0 = s, L = ctx > 0 ? 1 : 0;
+  if constexpr (MULTI) {
+    const int T = prm.num_query_tokens;
+    q0 = prm.query_start[s];
+    int qe = prm.query_start[s + 1];
+    q0 = q0 < 0 ? 0 : (q0 > T ? T : q0);
+    qe = qe < q0 ? q0 : (qe > T ? T : qe);
+    L = qe - q0;
+    L = L < ctx ? L : ctx;
+    L = L < prm.max_query_len ? L : prm.max_query_len;
+  } else if (ctx == 0) {
+    const size_t orow = ((size_t)s * Hq + (size_t)h * G + col) * D;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) store_out<DT>(prm.out, orow + lane + 64 * j, 0.f);
     return;
   }
-  const int nsub = prm.seq_prefix[prm.num_seqs];
-  const int chunk = stream_chunk(prm.num_kv_heads * nsub, prm.stream_wgs * kWaves);
-  const int A = h * nsub + prm.seq_prefix[s];
-  const int E = A + (ctx + kSub - 1) / kSub;
+  const int c = cg * kSub + col;
+  if (c >= L * G) return;
+  const size_t orow = ((size_t)(q0 + c / G) * Hq + (size_t)h * G + c % G) * D;
+  const int per = prm.seq_prefix[prm.num_seqs];
+  const int chunk = stream_chunk(prm.num_kv_heads * per, prm.stream_wgs * kWaves);
+  const int nsub = (ctx + kSub - 1) / kSub;
+  const int A = h * per + prm.seq_prefix[s] + cg * nsub;
+  const int E = A + nsub;
   const int k1 = A / chunk, k2 = (E - 1) / chunk;
   if (k1 == k2) return;  // one wave covered it and wrote `out`
-  // wave k's piece sits in its slot 0 unless the sequence starts inside chunk k1
+  // wave k's piece sits in its slot 0 unless the group starts inside chunk k1
   const int first_slot = k1 * 2 + (A != k1 * chunk ? 1 : 0);
-  auto row_of = [&](int k) -> size_t { return (size_t)(k == k1 ? first_slot : k * 2) * G + g; };
+  auto row_of = [&](int k) -> size_t { return (size_t)(k == k1 ? first_slot : k * 2) * cols + col; };
 
   float M = kNegInf;
   for (int k = k1 + lane; k <= k2; k += 64) M = fmaxf(M, prm.part_ml[row_of(k) * 2]);
@@ -939,14 +1069,27 @@ hipError_t launch_typed(const AttnParams& prm, hipStream_t stream) {
   const long long nout = (long long)prm.num_seqs * prm.num_q_heads;
   if (nout > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (prm.stream_wgs > 0) {
-    hipLaunchKernelGGL((attn_stream_kernel<DT, D, BS>), dim3((unsigned)prm.stream_wgs), block, 0,
-                       stream, prm);
+    const long long nmerge =
+        (long long)prm.num_seqs * prm.num_kv_heads * prm.max_groups * prm.slot_cols;
+    if (nmerge > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (prm.query_start) {
+      hipLaunchKernelGGL((attn_stream_kernel<DT, D, BS, true>), dim3((unsigned)prm.stream_wgs),
+                         block, 0, stream, prm);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL((attn_stream_merge_kernel<DT, D, true>), dim3((unsigned)nmerge), dim3(64),
+                         0, stream, prm);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL((attn_stream_kernel<DT, D, BS, false>), dim3((unsigned)prm.stream_wgs),
+                       block, 0, stream, prm);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((attn_stream_merge_kernel<DT, D>), dim3((unsigned)nout), dim3(64), 0,
-                       stream, prm);
+    hipLaunchKernelGGL((attn_stream_merge_kernel<DT, D, false>), dim3((unsigned)nmerge), dim3(64),
+                       0, stream, prm);
     return hipGetLastError();
   }
+  if (prm.query_start) return hipErrorInvalidValue;  // multi-token calls take the stream path
   const long long nwg = (long long)prm.num_seqs * prm.num_kv_heads * prm.max_partitions;
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
@@ -979,17 +1122,16 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-AttnWorkspace attn_workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+AttnWorkspace attn_workspace_layout(int32_t num_seqs, int32_t slot_cols, int32_t num_q_heads,
                                     int32_t head_dim, int32_t max_context_len, int32_t stream_wgs) {
   AttnWorkspace ws{0, 0, 0, 0};
-  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return ws;
+  if (num_seqs <= 0 || num_q_heads <= 0 || slot_cols <= 0 || head_dim <= 0) return ws;
   if (stream_wgs > 0) {
-    const size_t G = (size_t)(num_q_heads / num_kv_heads);
     const size_t slots = (size_t)stream_wgs * kWaves * 2;
     ws.prefix_off = 0;
     ws.part_o_off = align256(sizeof(int32_t) * ((size_t)num_seqs + 1));
-    ws.part_ml_off = align256(ws.part_o_off + slots * G * head_dim * sizeof(float));
-    ws.bytes = ws.part_ml_off + slots * G * 2 * sizeof(float);
+    ws.part_ml_off = align256(ws.part_o_off + slots * slot_cols * head_dim * sizeof(float));
+    ws.bytes = ws.part_ml_off + slots * slot_cols * 2 * sizeof(float);
     return ws;
   }
   const int32_t P = max_context_len <= 0 ? 1

@@ -22,6 +22,7 @@ constexpr int kSubTokens = 16;
 constexpr int kStreamWaves = 4;           // waves per workgroup
 constexpr int kMaxStreamSeqs = 4096;      // batch limit (per-sequence tables live in LDS)
 constexpr int kMinChunk = 4;              // sub-tiles per wave at least
+constexpr int kMaxMultiSeqs = 2048;       // batch limit with several new tokens per sequence
 // Positions (H_kv x sub-tiles of the batch) the stream path indexes in 32 bits;
 // the host sends calls whose bound B * ceil(max_ctx / 16) * H_kv exceeds it to
 // the grid path.
@@ -55,13 +56,22 @@ struct AttnParams {
   float* part_ml;
   int32_t stream_wgs;           // > 0: stream path with this many workgroups
   int32_t max_partitions;       // grid path: ceil(max_context_len / kPartitionTokens)
+  // Several new tokens per sequence (stream path only).  query_start [B+1]
+  // device prefix of query rows, or nullptr for decode (row s = sequence s).
+  // Columns of a sequence: (new token, query head) pairs in groups of 16.
+  const int32_t* query_start;
+  int32_t num_query_tokens;     // rows of q / out
+  int32_t max_query_len;        // host-known bound of the new tokens per sequence
+  int32_t max_groups;           // ceil(max_query_len * G / 16)
+  int32_t slot_cols;            // columns per partial slot: min(16, max_query_len * G)
 };
 
 // Workspace layout of one decode call, shared by the size query and the call.
 struct AttnWorkspace {
   size_t prefix_off, part_o_off, part_ml_off, bytes;
 };
-AttnWorkspace attn_workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+// slot_cols: columns per partial slot (min(16, max_query_len * G)).
+AttnWorkspace attn_workspace_layout(int32_t num_seqs, int32_t slot_cols, int32_t num_q_heads,
                                     int32_t head_dim, int32_t max_context_len, int32_t stream_wgs);
 
 // dtype: 0 f32, 1 f16, 2 bf16.  Returns hipErrorInvalidValue for a (dtype,

@@ -74,14 +74,25 @@ int stream_workgroups() {
 }
 
 // Workgroups of the stream path for this call on the current device, or 0
-// for the grid path (batches above kMaxStreamSeqs, or more positions than the
-// stream path indexes).
-int32_t stream_wgs_for(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
-  if (num_seqs > pkv::kMaxStreamSeqs) return 0;
+// where it cannot take the call: a batch above its LDS tables, or more
+// positions (kv heads x column groups x sub-tiles) than it indexes.  Decode
+// calls then take the grid path; multi-token calls are refused.
+int32_t stream_wgs_for(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                       int32_t max_groups, bool multi) {
+  if (num_seqs > (multi ? pkv::kMaxMultiSeqs : pkv::kMaxStreamSeqs)) return 0;
   const long long subs = ((long long)(max_context_len > 0 ? max_context_len : 0) + pkv::kSubTokens - 1) /
                          pkv::kSubTokens;
-  if ((long long)num_seqs * num_kv_heads * subs > pkv::kMaxStreamPositions) return 0;
+  if ((long long)num_seqs * num_kv_heads * max_groups * subs > pkv::kMaxStreamPositions) return 0;
   return stream_workgroups();
+}
+
+// Column geometry of a call: groups of 16 (new token, query head) columns.
+int32_t max_groups_for(int32_t max_query_len, int32_t group) {
+  return (int32_t)(((long long)max_query_len * group + pkv::kSubTokens - 1) / pkv::kSubTokens);
+}
+int32_t slot_cols_for(int32_t max_query_len, int32_t group) {
+  const long long c = (long long)max_query_len * group;
+  return (int32_t)(c < pkv::kSubTokens ? c : pkv::kSubTokens);
 }
 
 int32_t partitions_for(int32_t max_context_len) {
@@ -129,24 +140,36 @@ pkv_status paged_kv_append(const void* key, const void* value, void* k_cache, vo
   return err == hipSuccess ? PKV_OK : hip_fail(err, "paged_kv_append launch");
 }
 
-size_t paged_attention_workspace_bytes(pkv_pool pool, int32_t num_seqs, int32_t num_q_heads,
-                                       int32_t max_context_len) {
+}  // extern "C"
+
+namespace {
+
+// Workspace of a decode (max_query_len 1, multi false) or multi-token call,
+// or 0 with a reason for a call that is refused.
+size_t attention_workspace(const pkv_pool& pool, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t max_query_len, int32_t max_context_len, bool multi) {
   if (check_pool(pool) != PKV_OK || num_seqs <= 0 || num_q_heads <= 0 || max_context_len < 0 ||
-      num_q_heads % pool.num_kv_heads != 0)
+      max_query_len <= 0 || num_q_heads % pool.num_kv_heads != 0)
     return 0;
-  g_err[0] = '\0';
-  return pkv::attn_workspace_layout(num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim,
-                                    max_context_len, stream_wgs_for(num_seqs, pool.num_kv_heads, max_context_len))
+  const int32_t group = num_q_heads / pool.num_kv_heads;
+  const int32_t groups = max_groups_for(max_query_len, group);
+  const int32_t wgs = stream_wgs_for(num_seqs, pool.num_kv_heads, max_context_len, groups, multi);
+  if (multi && wgs == 0) return 0;
+  return pkv::attn_workspace_layout(num_seqs, slot_cols_for(max_query_len, group), num_q_heads,
+                                    pool.head_dim, max_context_len, wgs)
       .bytes;
 }
 
-pkv_status paged_attention_decode(void* out, const void* q, const void* k_cache,
-                                  const void* v_cache, pkv_pool pool,
-                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                  const int32_t* context_lens, int32_t num_seqs,
-                                  int32_t num_q_heads, float scale, int32_t max_context_len,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  g_err[0] = '\0';
+// Validation and launch shared by paged_attention_decode (query_start null:
+// row s is sequence s's one new token) and paged_attention_multi.
+pkv_status attention_call(const char* what, void* out, const void* q, const void* k_cache,
+                          const void* v_cache, const pkv_pool& pool, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          const int32_t* query_start, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_query_tokens, int32_t max_query_len, float scale,
+                          int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  const bool multi = query_start != nullptr;
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
   if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs %d < 0", num_seqs);
@@ -161,13 +184,27 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_cache,
     return fail(PKV_EINVAL, "max_blocks_per_seq %d * block_size %d < max_context_len %d",
                 max_blocks_per_seq, pool.block_size, max_context_len);
   if (!(scale == scale)) return fail(PKV_EINVAL, "scale is NaN");
+  if (multi) {
+    if (num_query_tokens < 0 || max_query_len < 0)
+      return fail(PKV_EINVAL, "num_query_tokens %d / max_query_len %d < 0", num_query_tokens,
+                  max_query_len);
+    if (num_query_tokens == 0 || max_query_len == 0) return PKV_OK;
+  }
   if (!out || !q || !k_cache || !v_cache || !context_lens || (max_blocks_per_seq > 0 && !block_tables))
     return fail(PKV_EINVAL, "null pointer argument");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_EINVAL, "out, q and the pools must be 16-byte aligned");
-  const int32_t stream_wgs = stream_wgs_for(num_seqs, pool.num_kv_heads, max_context_len);
+  const int32_t groups = max_groups_for(max_query_len, group);
+  const int32_t stream_wgs =
+      stream_wgs_for(num_seqs, pool.num_kv_heads, max_context_len, groups, multi);
+  if (multi && stream_wgs == 0)
+    return fail(PKV_EUNSUPPORTED,
+                "multi-token attention takes at most %d sequences and 2^28 positions "
+                "(kv heads x 16-column groups x 16-token sub-tiles)",
+                pkv::kMaxMultiSeqs);
+  const int32_t cols = slot_cols_for(max_query_len, group);
   const pkv::AttnWorkspace lay = pkv::attn_workspace_layout(
-      num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim, max_context_len, stream_wgs);
+      num_seqs, cols, num_q_heads, pool.head_dim, max_context_len, stream_wgs);
   if (lay.bytes > 0 && (!workspace || workspace_bytes < lay.bytes))
     return fail(PKV_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, lay.bytes);
   if (lay.bytes > 0 && !aligned16(workspace)) return fail(PKV_EINVAL, "workspace must be 16-byte aligned");
@@ -193,8 +230,57 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_cache,
   prm.part_ml = lay.bytes > 0 ? reinterpret_cast<float*>(base + lay.part_ml_off) : nullptr;
   prm.stream_wgs = stream_wgs;
   prm.max_partitions = partitions_for(max_context_len);
+  prm.query_start = query_start;
+  prm.num_query_tokens = multi ? num_query_tokens : num_seqs;
+  prm.max_query_len = multi ? max_query_len : 1;
+  prm.max_groups = groups;
+  prm.slot_cols = cols;
   hipError_t err = pkv::launch_paged_attention(prm, pool.dtype, pool.head_dim, pool.block_size, stream);
-  return err == hipSuccess ? PKV_OK : hip_fail(err, "paged_attention_decode launch");
+  return err == hipSuccess ? PKV_OK : hip_fail(err, what);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t paged_attention_workspace_bytes(pkv_pool pool, int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t max_context_len) {
+  g_err[0] = '\0';
+  return attention_workspace(pool, num_seqs, num_q_heads, 1, max_context_len, false);
+}
+
+pkv_status paged_attention_decode(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, pkv_pool pool,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, float scale, int32_t max_context_len,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = '\0';
+  return attention_call("paged_attention_decode launch", out, q, k_cache, v_cache, pool,
+                        block_tables, max_blocks_per_seq, context_lens, nullptr, num_seqs,
+                        num_q_heads, num_seqs, 1, scale, max_context_len, workspace,
+                        workspace_bytes, stream);
+}
+
+size_t paged_attention_multi_workspace_bytes(pkv_pool pool, int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t max_query_len, int32_t max_context_len) {
+  g_err[0] = '\0';
+  return attention_workspace(pool, num_seqs, num_q_heads, max_query_len, max_context_len, true);
+}
+
+pkv_status paged_attention_multi(void* out, const void* q, const void* k_cache,
+                                 const void* v_cache, pkv_pool pool, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 const int32_t* query_start, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_query_tokens, int32_t max_query_len, float scale,
+                                 int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  g_err[0] = '\0';
+  if (!query_start) return fail(PKV_EINVAL, "null pointer argument (query_start)");
+  return attention_call("paged_attention_multi launch", out, q, k_cache, v_cache, pool,
+                        block_tables, max_blocks_per_seq, context_lens, query_start, num_seqs,
+                        num_q_heads, num_query_tokens, max_query_len, scale, max_context_len,
+                        workspace, workspace_bytes, stream);
 }
 
 pkv_status paged_copy_blocks(void* k_cache, void* v_cache, pkv_pool pool,

@@ -21,6 +21,9 @@ The five named workloads (structure as stated with each builder):
                       unique suffixes of 16..512 tokens, 32/8 heads, D 128
   5 ``long_ctx``      32 sequences, 64/8 heads, D 128, log-uniform
                       [1024, 32768], block size 16 or 32
+Several new tokens per sequence:
+    ``spec_verify``   the Llama-3-8B GQA shape with 4 draft tokens per sequence
+    ``prefill_chunk`` 8 prompts each processing a 256-token chunk
 """
 
 import math
@@ -33,6 +36,7 @@ ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 NAN_BITS = {"f16": 0x7E00, "bf16": 0x7FC0}
 
 NAMED = ("tiny_f32", "llama2_7b_f16", "llama3_8b_gqa", "shared_prefix", "long_ctx")
+MULTI = ("spec_verify", "prefill_chunk")
 
 
 @dataclass
@@ -51,10 +55,23 @@ class Workload:
     slot_mapping: np.ndarray = field(default=None)    # [T] int32
     new_key: np.ndarray = field(default=None)         # [T, H_kv, D]
     new_value: np.ndarray = field(default=None)
+    # several new tokens per sequence: q holds [T, H_q, D] packed rows and
+    # query_start [B + 1] their prefix (None for decode: row s = sequence s)
+    query_start: np.ndarray = field(default=None)
+
+    @property
+    def multi(self):
+        return self.query_start is not None
+
+    @property
+    def max_query_len(self):
+        if not self.multi:
+            return 1
+        return int(np.diff(self.query_start).max()) if len(self.query_start) > 1 else 0
 
     @property
     def num_seqs(self):
-        return self.q.shape[0]
+        return self.context_lens.shape[0]
 
     @property
     def num_q_heads(self):
@@ -138,13 +155,15 @@ def _poison(pool, dtype):
 
 def build(name, seed, rng, ctx, H_q, H_kv, D, bs, dtype, scale=None,
           num_blocks=None, free_frac=0.10, max_blocks=None, append_last=True,
-          poison=False):
+          poison=False, query_lens=None):
     """Private blocks per sequence, drawn through one shuffled pool.
 
     ``ctx`` are the context lengths after the step.  With ``append_last`` the
     step appends each sequence's final token (position ctx-1) before attention.
-    ``poison`` fills every slot the step does not define (free blocks, tail
-    slots, the slots about to be appended) with NaN.
+    With ``query_lens`` (several new tokens per sequence) the step appends the
+    last query_lens[s] tokens of every sequence and q holds one packed row per
+    new token.  ``poison`` fills every slot the step does not define (free
+    blocks, tail slots, the slots about to be appended) with NaN.
     """
     ctx = np.asarray(ctx, dtype=np.int32)
     B = len(ctx)
@@ -160,10 +179,22 @@ def build(name, seed, rng, ctx, H_q, H_kv, D, bs, dtype, scale=None,
     for s in range(B):
         bt[s, :nbs[s]] = perm[nxt:nxt + nbs[s]]
         nxt += nbs[s]
-    q = _normal(rng, (B, H_q, D), dtype)
+    qstart = None
+    if query_lens is not None:
+        query_lens = np.asarray(query_lens, dtype=np.int32)
+        if np.any(query_lens > ctx) or np.any(query_lens < 0):
+            raise ValueError("need 0 <= query_lens <= ctx")
+        qstart = np.concatenate([[0], np.cumsum(query_lens)]).astype(np.int32)
+    q = _normal(rng, (B if qstart is None else int(qstart[-1]), H_q, D), dtype)
     k_cache = _normal(rng, (NB, H_kv, bs, D), dtype)
     v_cache = _normal(rng, (NB, H_kv, bs, D), dtype)
-    if append_last:
+    if qstart is not None:
+        slots = np.array([bt[s, t // bs] * bs + t % bs
+                          for s in range(B) for t in range(int(ctx[s]) - int(query_lens[s]),
+                                                           int(ctx[s]))], dtype=np.int32)
+        new_key = _normal(rng, (len(slots), H_kv, D), dtype)
+        new_value = _normal(rng, (len(slots), H_kv, D), dtype)
+    elif append_last:
         live = [s for s in range(B) if ctx[s] > 0]
         slots = np.array([bt[s, (ctx[s] - 1) // bs] * bs + (ctx[s] - 1) % bs for s in live],
                          dtype=np.int32)
@@ -190,7 +221,7 @@ def build(name, seed, rng, ctx, H_q, H_kv, D, bs, dtype, scale=None,
     return Workload(name=name, dtype=dtype, seed=seed, q=q, k_cache=k_cache,
                     v_cache=v_cache, block_tables=bt, context_lens=ctx, scale=float(scale),
                     block_mapping=np.zeros((0, 2), dtype=np.int32), slot_mapping=slots,
-                    new_key=new_key, new_value=new_value)
+                    new_key=new_key, new_value=new_value, query_start=qstart)
 
 
 # ---------------------------------------------------------------------------
@@ -294,6 +325,28 @@ def shared_prefix(seed=388004, poison=False, num_seqs=100, prefix_tokens=5000,
                     slot_mapping=slots, new_key=new_key, new_value=new_value)
 
 
+def spec_verify(seed=388006, poison=False, num_seqs=128, draft=4):
+    """Speculative-decode verification on the Llama-3-8B-shaped GQA layer: the
+    same shape and context distribution as ``llama3_8b_gqa`` (32 query / 8 KV
+    heads of 128, bf16, contexts log-uniform in [256, 8192]), with ``draft``
+    guessed tokens per sequence appended and attended at once (4 tokens x 4
+    query heads per KV head = 16 MFMA columns)."""
+    rng = np.random.default_rng(seed)
+    ctx = log_uniform_lengths(rng, num_seqs, 256, 8192)
+    return build("spec_verify", seed, rng, ctx, 32, 8, 128, 16, "bf16", max_blocks=512,
+                 poison=poison, query_lens=np.full(num_seqs, draft, dtype=np.int32))
+
+
+def prefill_chunk(seed=388007, poison=False, num_seqs=8, chunk=256):
+    """Chunked prefill on the Llama-3-8B-shaped GQA layer: ``num_seqs``
+    prompts, each processing a chunk of ``chunk`` new tokens on top of an
+    earlier context (total contexts uniform in [chunk, 4096]), bf16."""
+    rng = np.random.default_rng(seed)
+    ctx = uniform_lengths(rng, num_seqs, chunk, 4096)
+    return build("prefill_chunk", seed, rng, ctx, 32, 8, 128, 16, "bf16", max_blocks=256,
+                 poison=poison, query_lens=np.full(num_seqs, chunk, dtype=np.int32))
+
+
 def named(name, **kw):
     """Build a named workload: one of NAMED, or ``long_ctx_bs16``/``long_ctx_bs32``."""
     if name == "tiny_f32":
@@ -308,4 +361,8 @@ def named(name, **kw):
         return long_ctx(block_size=16, **kw)
     if name == "long_ctx_bs32":
         return long_ctx(block_size=32, **kw)
+    if name == "spec_verify":
+        return spec_verify(**kw)
+    if name == "prefill_chunk":
+        return prefill_chunk(**kw)
     raise KeyError(name)

@@ -72,8 +72,14 @@ class DeviceWorkload:
         self.new_key = to_dev(w.new_key, d, dev)
         self.new_value = to_dev(w.new_value, d, dev)
         self.out = torch.empty_like(self.q)
-        need = _lib.paged_attention_workspace_bytes(self.k_cache, w.num_seqs, w.num_q_heads,
-                                                    w.max_context_len)
+        self.query_start = None
+        if w.multi:
+            self.query_start = to_dev(w.query_start.astype(np.int32), d, dev)
+            need = _lib.paged_attention_multi_workspace_bytes(
+                self.k_cache, w.num_seqs, w.num_q_heads, w.max_query_len, w.max_context_len)
+        else:
+            need = _lib.paged_attention_workspace_bytes(self.k_cache, w.num_seqs, w.num_q_heads,
+                                                        w.max_context_len)
         self.workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
 
     def write_step(self):
@@ -84,9 +90,15 @@ class DeviceWorkload:
                                  self.slot_mapping)
 
     def attend(self):
-        _lib.paged_attention_decode(self.out, self.q, self.k_cache, self.v_cache,
-                                    self.block_tables, self.context_lens, self.w.scale,
-                                    self.w.max_context_len, self.workspace)
+        if self.w.multi:
+            _lib.paged_attention_multi(self.out, self.q, self.k_cache, self.v_cache,
+                                       self.block_tables, self.context_lens, self.query_start,
+                                       self.w.scale, self.w.max_context_len,
+                                       max(1, self.w.max_query_len), self.workspace)
+        else:
+            _lib.paged_attention_decode(self.out, self.q, self.k_cache, self.v_cache,
+                                        self.block_tables, self.context_lens, self.w.scale,
+                                        self.w.max_context_len, self.workspace)
         return self.out
 
     def step(self):
@@ -105,5 +117,9 @@ def oracle_pools_after_step(w):
 
 def oracle_step(w, seq_ids=None, pools=None):
     kc, vc = pools if pools is not None else oracle_pools_after_step(w)
+    if w.multi:
+        assert seq_ids is None
+        return oracle.multi_query_attention(w.q, kc, vc, w.block_tables, w.context_lens,
+                                            np.diff(w.query_start), w.scale, w.dtype)
     return oracle.decode_attention(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
                                    w.dtype, seq_ids=seq_ids)

@@ -1,0 +1,103 @@
+"""Multi-token paged attention (several new tokens per sequence) on the GPU
+against the CPU oracle, through the C ABI (needs an MI355X).
+
+Ragged numbers of new tokens per sequence, every dtype / head_dim /
+block_size, query-head groups of 1 to 16, column groups beyond one MFMA tile
+(L * G > 16), whole-context chunks (L = n), empty sequences, NaN-poisoned
+pools; bit-identical results under a physical permutation of the pool.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_388_amd import _lib
+from paged_kv_cache_388_amd import workloads as wl
+
+from gpu_common import DeviceWorkload, check_attention, oracle_step, to_host
+
+pytestmark = pytest.mark.gpu
+
+CTX = [1, 5, 16, 17, 40, 300, 513, 700]
+QLENS = [1, 5, 3, 17, 0, 7, 16, 2]
+
+
+def _run(w, what):
+    print(f"[gpu] {what}: B={w.num_seqs} T={w.q.shape[0]} Hq={w.num_q_heads} "
+          f"Hkv={w.num_kv_heads} D={w.head_dim} bs={w.block_size} {w.dtype} "
+          f"maxq={w.max_query_len} maxctx={w.max_context_len}", flush=True)
+    dw = DeviceWorkload(w)
+    out = dw.step()
+    torch.cuda.synchronize()
+    return check_attention(to_host(out, w.dtype), oracle_step(w), w.dtype, what)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_multi_grid(dtype, D, bs, G):
+    rng = np.random.default_rng(41)
+    w = wl.build(f"multi_{dtype}_{D}_{bs}_{G}", 41, rng, CTX, 2 * G, 2, D, bs, dtype,
+                 poison=True, query_lens=QLENS)
+    _run(w, f"multi {dtype} D{D} bs{bs} G{G}")
+
+
+@pytest.mark.parametrize("G", [3, 16])
+def test_multi_other_groups(G):
+    rng = np.random.default_rng(42)
+    w = wl.build(f"multi_G{G}", 42, rng, [9, 130, 600], G, 1, 128, 16, "bf16", poison=True,
+                 query_lens=[9, 4, 11])
+    _run(w, f"multi G{G}")
+
+
+def test_whole_context_chunks():
+    rng = np.random.default_rng(43)
+    ctx = [1, 16, 33, 64]
+    w = wl.build("whole", 43, rng, ctx, 8, 2, 128, 16, "bf16", poison=True, query_lens=ctx)
+    _run(w, "L = n")
+
+
+def test_one_token_each_matches_decode_bitwise():
+    rng = np.random.default_rng(44)
+    ctx = [3, 200, 900, 2100]
+    w = wl.build("one", 44, rng, ctx, 16, 4, 128, 16, "bf16", query_lens=[1, 1, 1, 1])
+    multi = to_host(DeviceWorkload(w).step(), "bf16")
+    w.query_start = None
+    dec = to_host(DeviceWorkload(w).step(), "bf16")
+    assert np.array_equal(multi, dec)
+
+
+def test_physical_permutation_invariance_bitwise():
+    rng = np.random.default_rng(45)
+    w = wl.build("perm", 45, rng, [20, 600, 1500], 32, 8, 128, 16, "bf16", query_lens=[4, 4, 4])
+    base = to_host(DeviceWorkload(w).step(), "bf16")
+    dw = DeviceWorkload(w)
+    dw.write_step()
+    kc, vc = to_host(dw.k_cache, "bf16"), to_host(dw.v_cache, "bf16")
+    pi = np.random.default_rng(46).permutation(kc.shape[0])
+    kp, vp = np.empty_like(kc), np.empty_like(vc)
+    kp[pi], vp[pi] = kc, vc
+    bt = np.where(w.block_tables >= 0, pi[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
+    w2 = wl.Workload(name="perm2", dtype="bf16", seed=0, q=w.q, k_cache=kp, v_cache=vp,
+                     block_tables=bt, context_lens=w.context_lens, scale=w.scale,
+                     block_mapping=np.zeros((0, 2), np.int32), slot_mapping=np.zeros((0,), np.int32),
+                     new_key=w.new_key[:0], new_value=w.new_value[:0], query_start=w.query_start)
+    moved = to_host(DeviceWorkload(w2).step(), "bf16")
+    assert np.array_equal(base, moved)
+
+
+def test_too_many_sequences_refused():
+    rng = np.random.default_rng(47)
+    w = wl.build("big", 47, rng, np.full(2049, 2), 4, 1, 64, 16, "f16",
+                 query_lens=np.full(2049, 1))
+    dw = DeviceWorkload(w)
+    with pytest.raises(_lib.PagedKVError):
+        dw.attend()
+
+
+@pytest.mark.parametrize("name", ["spec_verify", "prefill_chunk"])
+def test_full_size_multi_workloads(name):
+    w = wl.named(name)
+    err = _run(w, name)
+    print(f"[gpu] {name}: max |gpu - oracle| = {err:.3e}", flush=True)

@@ -61,6 +61,8 @@ def test_partition_and_workspace_arithmetic(lib):
 def test_status_strings(lib):
     for code in range(6):
         assert lib.pkv_status_string(code)
+    # every entry point clears the calling thread's message; one that succeeds leaves it empty
+    assert lib.paged_kv_append(None, None, None, None, _pool(), None, 0, None) == 0
     assert lib.pkv_last_error() == b""
 
 
