@@ -238,6 +238,79 @@ PKV_API pkv_status pkv_stream_copy(void* dst, const void* src, size_t bytes,
 PKV_API pkv_status pkv_stream_read(const void* src, size_t bytes, uint32_t* sink,
                                    hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Host block manager (host memory only; no device work).
+ *
+ * The pool's free list, per-block reference counts and per-sequence block
+ * tables, grown on demand: a sequence takes one more block only when its last
+ * block is full, and freed blocks return to the pool ("Optimizing LLM
+ * Inference: From PagedAttention to AI Infra", "On-Demand Allocation"; "05
+ * PagedAttention", "Managing Virtual Memory (Block Manager)").  A fork shares
+ * its parent's blocks; appending to a shared, partly filled last block first
+ * copies it (copy-on-write: the pair is returned for paged_copy_blocks) while
+ * the shared block stays unchanged (first page, "Copy-on-Write"; "05
+ * PagedAttention", "KV Cache Sharing (Copy-on-Write)").  With the prefix
+ * cache on, every block that fills is remembered under a 128-bit hash chain
+ * of the token ids of the whole prefix it ends, and a new sequence reuses its
+ * longest run of remembered leading full blocks (the second page, "Prefix
+ * Caching"; "The Memory Wall", "Sharing is Caring: Prefix Caching").
+ *
+ * Policy: the lowest-numbered free block that holds no remembered prefix is
+ * taken first; then the remembered free block released longest ago is
+ * evicted and reused; a sequence's blocks are released last block first; a
+ * prompt never reuses the block of its last token; an add or append the pool
+ * cannot hold returns PKV_EWORKSPACE and changes nothing.  Slots are
+ * block * block_size + offset, as paged_kv_append takes them.  One manager
+ * must not be used by two threads at once.  Errors: pkv_bm_last_error().
+ * ------------------------------------------------------------------------ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+typedef struct {
+  int64_t blocks_in_use;   /* blocks with a reference */
+  int64_t tokens_stored;   /* token slots holding a token, over distinct blocks */
+  int64_t slots_reserved;  /* blocks_in_use * block_size */
+  int64_t cached_blocks;   /* blocks remembered by the prefix cache (used or free) */
+  int64_t free_blocks;     /* blocks an allocation can take */
+  int64_t num_sequences;
+} pkv_bm_stats;
+
+/* NULL on invalid sizes (num_blocks * block_size must be < 2^31) or no memory. */
+PKV_API pkv_block_manager* pkv_bm_create(int32_t num_blocks, int32_t block_size,
+                                         int32_t prefix_cache);
+PKV_API void pkv_bm_destroy(pkv_block_manager* bm);
+PKV_API const char* pkv_bm_last_error(void);
+PKV_API int32_t pkv_bm_num_free_blocks(const pkv_block_manager* bm);
+
+/* New sequence with its prompt (host array of num_tokens token ids).  Writes
+ * *num_reused (leading prompt tokens found in the prefix cache, a multiple of
+ * block_size) and slots[num_tokens]: -1 for reused tokens (their K/V already
+ * sit in shared blocks), else the slot the token's K/V go to. */
+PKV_API pkv_status pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id,
+                                       const int32_t* tokens, int32_t num_tokens,
+                                       int32_t* num_reused, int32_t* slots);
+
+/* Append num_tokens new tokens: writes slots[num_tokens]; when the last block
+ * was shared and partly filled, *num_cow = 1 and cow_pair = {src, dst} must be
+ * copied (paged_copy_blocks) before the new tokens are written; else
+ * *num_cow = 0. */
+PKV_API pkv_status pkv_bm_append(pkv_block_manager* bm, int64_t seq_id, const int32_t* tokens,
+                                 int32_t num_tokens, int32_t* slots, int32_t* cow_pair,
+                                 int32_t* num_cow);
+
+/* child shares all of parent's blocks (parallel sampling, beam search). */
+PKV_API pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
+PKV_API pkv_status pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq_id);
+PKV_API pkv_status pkv_bm_sequence_info(const pkv_block_manager* bm, int64_t seq_id,
+                                        int32_t* num_tokens, int32_t* num_blocks);
+
+/* block_tables [num_seqs, max_blocks_per_seq] (-1 past each sequence's
+ * blocks) and context_lens [num_seqs] of the listed sequences, host arrays
+ * ready for paged_attention_decode once copied to the device. */
+PKV_API pkv_status pkv_bm_build_batch(const pkv_block_manager* bm, const int64_t* seq_ids,
+                                      int32_t num_seqs, int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, int32_t* context_lens);
+PKV_API pkv_status pkv_bm_get_stats(const pkv_block_manager* bm, pkv_bm_stats* out);
+
 PKV_API const char* pkv_status_string(pkv_status status);
 /* Message of the calling thread's last failed call ("" if none). */
 PKV_API const char* pkv_last_error(void);

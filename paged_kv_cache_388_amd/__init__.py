@@ -7,6 +7,7 @@ Importing the package loads nothing; the library is loaded on first use.
 """
 
 from ._lib import (  # noqa: F401
+    BlockManager,
     PagedKVError,
     paged_attention_decode,
     paged_attention_multi,

@@ -245,3 +245,130 @@ def pkv_stream_read(src, sink, stream=None):
         raise ValueError("sink must hold 2048 32-bit words")
     _check(load().pkv_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
                                   _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# host block manager (pkv_bm_*)
+# ---------------------------------------------------------------------------
+
+class PkvBmStats(ctypes.Structure):
+    _fields_ = [("blocks_in_use", ctypes.c_int64), ("tokens_stored", ctypes.c_int64),
+                ("slots_reserved", ctypes.c_int64), ("cached_blocks", ctypes.c_int64),
+                ("free_blocks", ctypes.c_int64), ("num_sequences", ctypes.c_int64)]
+
+
+def _bm_lib():
+    lib = load()
+    if getattr(lib, "_bm_ready", False):
+        return lib
+    c_i32, c_i64, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    lib.pkv_bm_create.argtypes = [c_i32, c_i32, c_i32]
+    lib.pkv_bm_create.restype = c_vp
+    lib.pkv_bm_destroy.argtypes = [c_vp]
+    lib.pkv_bm_destroy.restype = None
+    lib.pkv_bm_last_error.argtypes = []
+    lib.pkv_bm_last_error.restype = ctypes.c_char_p
+    lib.pkv_bm_num_free_blocks.argtypes = [c_vp]
+    lib.pkv_bm_num_free_blocks.restype = c_i32
+    lib.pkv_bm_add_sequence.argtypes = [c_vp, c_i64, c_vp, c_i32, c_vp, c_vp]
+    lib.pkv_bm_add_sequence.restype = c_i32
+    lib.pkv_bm_append.argtypes = [c_vp, c_i64, c_vp, c_i32, c_vp, c_vp, c_vp]
+    lib.pkv_bm_append.restype = c_i32
+    lib.pkv_bm_fork.argtypes = [c_vp, c_i64, c_i64]
+    lib.pkv_bm_fork.restype = c_i32
+    lib.pkv_bm_free_sequence.argtypes = [c_vp, c_i64]
+    lib.pkv_bm_free_sequence.restype = c_i32
+    lib.pkv_bm_sequence_info.argtypes = [c_vp, c_i64, c_vp, c_vp]
+    lib.pkv_bm_sequence_info.restype = c_i32
+    lib.pkv_bm_build_batch.argtypes = [c_vp, c_vp, c_i32, c_vp, c_i32, c_vp]
+    lib.pkv_bm_build_batch.restype = c_i32
+    lib.pkv_bm_get_stats.argtypes = [c_vp, ctypes.POINTER(PkvBmStats)]
+    lib.pkv_bm_get_stats.restype = c_i32
+    lib._bm_ready = True
+    return lib
+
+
+class BlockManager:
+    """The library's host block manager (pkv_bm_* in include/pagedkv.h).
+    Host-side only: it hands out slots, copy-on-write pairs and block tables
+    for the device calls.  Methods raise PagedKVError (status PKV_EWORKSPACE
+    when the pool is exhausted, nothing changed)."""
+
+    def __init__(self, num_blocks, block_size, prefix_cache=True):
+        import numpy as np
+        self._np = np
+        self._lib = _bm_lib()
+        self._h = self._lib.pkv_bm_create(int(num_blocks), int(block_size), int(bool(prefix_cache)))
+        if not self._h:
+            raise PagedKVError(1, self._lib.pkv_bm_last_error().decode())
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def close(self):
+        if self._h:
+            self._lib.pkv_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _ok(self, status):
+        if status != 0:
+            raise PagedKVError(status, self._lib.pkv_bm_last_error().decode())
+
+    def _i32(self, a):
+        return self._np.ascontiguousarray(a, dtype=self._np.int32)
+
+    def num_free(self):
+        return int(self._lib.pkv_bm_num_free_blocks(self._h))
+
+    def add_sequence(self, seq_id, tokens):
+        """Returns (reused leading tokens, slots [n] int32 with -1 where reused)."""
+        t = self._i32(tokens)
+        slots = self._np.empty(len(t), dtype=self._np.int32)
+        reused = ctypes.c_int32(0)
+        self._ok(self._lib.pkv_bm_add_sequence(self._h, int(seq_id), t.ctypes.data, len(t),
+                                               ctypes.byref(reused), slots.ctypes.data))
+        return int(reused.value), slots
+
+    def append(self, seq_id, tokens):
+        """Returns (slots [k] int32, (src, dst) copy-on-write pair or None)."""
+        t = self._i32(tokens)
+        slots = self._np.empty(len(t), dtype=self._np.int32)
+        cow = self._np.zeros(2, dtype=self._np.int32)
+        ncow = ctypes.c_int32(0)
+        self._ok(self._lib.pkv_bm_append(self._h, int(seq_id), t.ctypes.data, len(t),
+                                         slots.ctypes.data, cow.ctypes.data, ctypes.byref(ncow)))
+        return slots, ((int(cow[0]), int(cow[1])) if ncow.value else None)
+
+    def fork(self, parent, child):
+        self._ok(self._lib.pkv_bm_fork(self._h, int(parent), int(child)))
+
+    def free_sequence(self, seq_id):
+        self._ok(self._lib.pkv_bm_free_sequence(self._h, int(seq_id)))
+
+    def sequence_info(self, seq_id):
+        n, nb = ctypes.c_int32(0), ctypes.c_int32(0)
+        self._ok(self._lib.pkv_bm_sequence_info(self._h, int(seq_id), ctypes.byref(n),
+                                                ctypes.byref(nb)))
+        return int(n.value), int(nb.value)
+
+    def build_batch(self, seq_ids, max_blocks_per_seq):
+        """Returns (block_tables [B, max_blocks] int32, context_lens [B] int32)."""
+        ids = self._np.ascontiguousarray(seq_ids, dtype=self._np.int64)
+        bt = self._np.empty((len(ids), int(max_blocks_per_seq)), dtype=self._np.int32)
+        lens = self._np.empty(len(ids), dtype=self._np.int32)
+        self._ok(self._lib.pkv_bm_build_batch(self._h, ids.ctypes.data, len(ids), bt.ctypes.data,
+                                              int(max_blocks_per_seq), lens.ctypes.data))
+        return bt, lens
+
+    def stats(self):
+        st = PkvBmStats()
+        self._ok(self._lib.pkv_bm_get_stats(self._h, ctypes.byref(st)))
+        d = {k: int(getattr(st, k)) for k, _ in PkvBmStats._fields_}
+        d["waste"] = ((d["slots_reserved"] - d["tokens_stored"]) / d["slots_reserved"]
+                      if d["slots_reserved"] else 0.0)
+        return d
