@@ -125,6 +125,187 @@ def cpu_baseline(w, min_seconds):
             "seqs_per_s": round(seqs / dt, 2)}
 
 
+def block_manager_trace(seed=388008, num_seqs=256, system_tokens=1000, steps=256):
+    """Serving-style bookkeeping trace: num_seqs prompts sharing a
+    system_tokens-token system prompt plus their own 16..256 tokens, then
+    `steps` decode steps appending one token to every sequence; every 32 steps
+    a quarter of the sequences is freed and replaced by new ones, and every 16
+    steps some sequences fork (parallel sampling)."""
+    rng = np.random.default_rng(seed)
+    system = [int(t) for t in rng.integers(0, 32000, size=system_tokens)]
+    ops = []
+    next_id = 0
+    live = []
+    for _ in range(num_seqs):
+        ops.append(("add", next_id, system + [int(t) for t in rng.integers(0, 32000, size=int(rng.integers(16, 257)))]))
+        live.append(next_id)
+        next_id += 1
+    for step in range(steps):
+        if step and step % 32 == 0:
+            for sid in list(rng.choice(live, size=len(live) // 4, replace=False)):
+                ops.append(("free", int(sid), None))
+                live.remove(int(sid))
+                ops.append(("add", next_id, system + [int(t) for t in rng.integers(0, 32000, size=int(rng.integers(16, 257)))]))
+                live.append(next_id)
+                next_id += 1
+        if step and step % 16 == 0:
+            for sid in list(rng.choice(live, size=4, replace=False)):
+                ops.append(("fork", int(sid), next_id))
+                live.append(next_id)
+                next_id += 1
+        ops.append(("step", [int(t) for t in rng.integers(0, 32000, size=len(live))], list(live)))
+    return ops
+
+
+def run_block_manager_trace(mgr, ops, max_blocks, seconds=None):
+    """Replay the trace on a manager (the library's or the model) until its end
+    or, with `seconds`, until that much time has passed.  Returns a dict of
+    counts and of the time spent in decode steps (one token for every live
+    sequence plus the step's block tables) and in the other operations."""
+    r = {"steps": 0, "ops": 0, "adds": 0, "reused": 0, "cows": 0, "step_s": 0.0, "add_s": 0.0,
+         "other_s": 0.0}
+    t_start = time.perf_counter()
+    for op in ops:
+        t0 = time.perf_counter()
+        if op[0] == "add":
+            r["reused"] += mgr.add_sequence(op[1], op[2])[0]
+            r["adds"] += 1
+        elif op[0] == "free":
+            mgr.free_sequence(op[1])
+        elif op[0] == "fork":
+            mgr.fork(op[1], op[2])
+        else:
+            r["cows"] += len(mgr.append_step(op[2], op[1])[1])
+            if hasattr(mgr, "build_batch"):
+                mgr.build_batch(op[2], max_blocks)
+            else:
+                for sid in op[2]:
+                    mgr.block_table(sid)
+            r["steps"] += 1
+        dt = time.perf_counter() - t0
+        r[{"step": "step_s", "add": "add_s"}.get(op[0], "other_s")] += dt
+        r["ops"] += 1
+        if seconds is not None and time.perf_counter() - t_start > seconds:
+            break
+    return r
+
+
+def block_manager_bench(cpu_seconds):
+    """Host bookkeeping of the decode loop: the library's block manager on a
+    serving-style trace.  The value is the mean time of one decode step's
+    bookkeeping (one token appended to every live sequence with its
+    copy-on-write pairs, then the step's block tables and lengths)."""
+    from paged_kv_cache_388_amd import _lib
+    ops = block_manager_trace()
+    nb, bs, max_blocks = 40000, 16, 128
+    mgr = _lib.BlockManager(nb, bs)
+    r = run_block_manager_trace(mgr, ops, max_blocks)
+    st = mgr.stats()
+    live = [op for op in ops if op[0] == "step"][-1][2]
+    line = {"metric": "block manager: host microseconds per decode step",
+            "value": round(r["step_s"] / r["steps"] * 1e6, 2), "unit": "us/step",
+            "higher_is_better": False, "steps": r["steps"], "data": "synthetic",
+            "config": {"workload": "block_manager_trace", "num_blocks": nb, "block_size": bs,
+                       "live_sequences_at_end": len(live), "system_prompt_tokens": 1000,
+                       "step": "pkv_bm_append_step + pkv_bm_build_batch through the Python binding"},
+            "add_sequence_us_mean": round(r["add_s"] / max(r["adds"], 1) * 1e6, 2),
+            "sequences_added": r["adds"], "reused_prompt_tokens": r["reused"],
+            "copy_on_write_pairs": r["cows"],
+            "blocks_in_use": st["blocks_in_use"], "tokens_stored": st["tokens_stored"],
+            "waste": round(st["waste"], 5), "cached_blocks": st["cached_blocks"]}
+    if cpu_seconds > 0:
+        import oracle.block_manager as obm
+        m = run_block_manager_trace(obm.BlockManagerModel(nb, bs), ops, max_blocks,
+                                    seconds=cpu_seconds)
+        line["cpu_baseline"] = {
+            "value": round(m["step_s"] / max(m["steps"], 1) * 1e6, 1), "unit": "us/step",
+            "cores": 1, "kind": "oracle",
+            "sample": f"the Python model on the first {m['ops']} operations ({m['steps']} decode "
+                      f"steps) of the same trace, {m['step_s'] + m['add_s'] + m['other_s']:.1f} s"}
+    print(json.dumps(line))
+
+
+def swap_bench(steps, warmup, cpu_seconds):
+    """Swap of a preempted batch between the pool and pinned host memory: a
+    Llama-3-8B-shaped layer pool (bf16, 8 KV heads, 16-token blocks, D=128) of
+    8192 blocks, 2048 scattered blocks (eight 4096-token contexts, 128 MiB of
+    K+V) out to host and back into other blocks, with the library's default
+    64 MiB staging.  Rates are bytes of K+V moved per second, PCIe included,
+    beside a plain contiguous device<->pinned copy of the same size."""
+    import torch
+    from paged_kv_cache_388_amd import _lib
+    _lib.load()
+    NB, H, BS, D, n = 8192, 8, 16, 128, 2048
+    g = torch.Generator(device="cuda")
+    g.manual_seed(388009)
+    kc = torch.empty((NB, H, BS, D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    kc.view(torch.int16).random_(-32768, 32767, generator=g)
+    vc.view(torch.int16).random_(-32768, 32767, generator=g)
+    rng = np.random.default_rng(388009)
+    perm = rng.permutation(NB).astype(np.int32)
+    out_ids = torch.from_numpy(perm[:n].copy()).cuda()
+    in_ids = torch.from_numpy(perm[n:2 * n].copy()).cuda()
+    moved = n * 2 * H * BS * D * 2
+    image = torch.empty((n, 2, H, BS, D), dtype=torch.bfloat16, pin_memory=True)
+    staging = torch.empty(_lib.SWAP_STAGING_BYTES, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for i in range(steps):
+            a[i].record(stream)
+            fn()
+            b[i].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([x.elapsed_time(y) for x, y in zip(a, b)]))
+
+    ms_out = timed(lambda: _lib.paged_swap_out(kc, vc, out_ids, host_image=image, staging=staging))
+    ms_in = timed(lambda: _lib.paged_swap_in(image, kc, vc, in_ids, staging=staging))
+    # the round trip moved out_ids' blocks into in_ids' blocks (bit patterns:
+    # the random pools hold NaNs)
+    for c in (kc.view(torch.int16), vc.view(torch.int16)):
+        assert torch.equal(c[in_ids.long()], c[out_ids.long()])
+    dev_flat = torch.empty(moved, dtype=torch.uint8, device="cuda")
+    host_flat = torch.empty(moved, dtype=torch.uint8, pin_memory=True)
+    ms_d2h = timed(lambda: host_flat.copy_(dev_flat, non_blocking=True))
+    ms_h2d = timed(lambda: dev_flat.copy_(host_flat, non_blocking=True))
+    gbs = lambda ms: round(moved / (ms * 1e-3) / 1e9, 2)
+    line = {"metric": "swap out / in of a preempted batch (K+V bytes moved per second)",
+            "value": gbs(ms_out), "unit": "GB/s", "higher_is_better": True, "steps": steps,
+            "warmup": warmup, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "swap_llama3_8b_layer", "pool_blocks": NB, "num_kv_heads": H,
+                       "block_size": BS, "head_dim": D, "blocks_moved": n,
+                       "staging_bytes": _lib.SWAP_STAGING_BYTES},
+            "swap_out_ms": round(ms_out, 3), "swap_out_GBps": gbs(ms_out),
+            "swap_in_ms": round(ms_in, 3), "swap_in_GBps": gbs(ms_in),
+            "plain_d2h_GBps": gbs(ms_d2h), "plain_h2d_GBps": gbs(ms_h2d),
+            "swap_out_vs_plain_copy": round(ms_d2h / ms_out, 3),
+            "swap_in_vs_plain_copy": round(ms_h2d / ms_in, 3)}
+    if cpu_seconds > 0:
+        import oracle
+        kh = kc.view(torch.int16).cpu().numpy().view(np.uint16)
+        vh = vc.view(torch.int16).cpu().numpy().view(np.uint16)
+        ids = perm[:n]
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.swap_out(kh, vh, ids)
+            reps += 1
+            if time.perf_counter() - t0 > cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(reps * moved / dt / 1e9, 2), "unit": "GB/s",
+                                "cores": 1, "kind": "oracle",
+                                "sample": f"oracle swap_out of the same {n} blocks from host "
+                                          f"arrays, {reps} repetitions in {dt:.1f} s"}
+    print(json.dumps(line))
+
+
 def copy_probe(mib, steps, warmup):
     """Time the library's plain 16-byte-vector copy: its duration gives the
     achievable read+write rate, and its FETCH_SIZE / WRITE_SIZE counters per
@@ -193,6 +374,11 @@ def main():
     ap.add_argument("--read-probe-mib", type=int, default=0,
                     help="instead of the decode step, time pkv_stream_read of this many MiB "
                          "(the achievable read-bandwidth reference)")
+    ap.add_argument("--swap", action="store_true",
+                    help="instead of the decode step, time swap out / in of a preempted batch")
+    ap.add_argument("--block-manager", action="store_true",
+                    help="instead of the decode step, time the host block manager on a "
+                         "serving-style trace")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the decode step, time pkv_stream_copy of this many MiB "
                          "(the reference copy for bandwidth and HBM counter calibration)")
@@ -203,6 +389,12 @@ def main():
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
+    if args.block_manager:
+        block_manager_bench(args.cpu_seconds)
+        return
+    if args.swap:
+        swap_bench(args.steps, args.warmup, args.cpu_seconds)
+        return
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib, args.steps, args.warmup)
         return

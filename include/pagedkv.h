@@ -222,6 +222,41 @@ PKV_API pkv_status paged_copy_blocks(void* k_cache, void* v_cache, pkv_pool pool
                                      hipStream_t stream);
 
 /*
+ * paged_swap_out / paged_swap_in — move blocks to host memory and back when
+ * the pool runs short ("The Memory Wall", "The Infrastructure Impact: Scale
+ * and Complexity", item "The Block Manager"; "05 PagedAttention", "Managing
+ * Virtual Memory (Block Manager)": inactive blocks go to CPU RAM and return
+ * when needed).
+ *
+ *   block_ids     [num_ids] int32 on the device.  Out: the blocks to copy, in
+ *                 order (an id outside the pool gives an all-zero entry).  In:
+ *                 the destination of each entry; they must be distinct (else
+ *                 the result depends on scheduling); an id outside the pool
+ *                 is skipped.
+ *   host_image    HOST memory of num_ids entries of 2 * block_bytes bytes,
+ *                 block_bytes = num_kv_heads * block_size * head_dim * element
+ *                 size: entry i is block_ids[i]'s K tile then its V tile, each
+ *                 [num_kv_heads, block_size, head_dim] ([num_ids, 2, H_kv, bs,
+ *                 D] in all).  Pinned memory (hipHostMalloc) keeps the copies
+ *                 asynchronous; pageable memory works but blocks the caller.
+ *   staging       DEVICE scratch of staging_bytes >= 2 * block_bytes (else
+ *                 PKV_EWORKSPACE); no initialisation needed.  Blocks move in
+ *                 runs of floor(staging_bytes / (2 * block_bytes)): a gather
+ *                 kernel packs a run into staging and one hipMemcpyAsync
+ *                 moves it to the host (paged_swap_in: the copy, then a
+ *                 scatter kernel).  Larger staging, fewer and larger copies.
+ *   num_ids       >= 0 (0 enqueues nothing)
+ * All work is enqueued on `stream`; host_image (out) or the pools (in) are
+ * complete when the stream reaches the end of it.  Raw bit copies.
+ */
+PKV_API pkv_status paged_swap_out(const void* k_cache, const void* v_cache, pkv_pool pool,
+                                  const int32_t* block_ids, int32_t num_ids, void* host_image,
+                                  void* staging, size_t staging_bytes, hipStream_t stream);
+PKV_API pkv_status paged_swap_in(const void* host_image, int32_t num_ids, void* k_cache,
+                                 void* v_cache, pkv_pool pool, const int32_t* block_ids,
+                                 void* staging, size_t staging_bytes, hipStream_t stream);
+
+/*
  * pkv_stream_copy — plain device-to-device copy of `bytes` bytes (a multiple
  * of 16) with 16-byte vector loads and stores.  A bandwidth and counter
  * reference for the kernels above, not part of the attention method.
@@ -296,6 +331,31 @@ PKV_API pkv_status pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id,
 PKV_API pkv_status pkv_bm_append(pkv_block_manager* bm, int64_t seq_id, const int32_t* tokens,
                                  int32_t num_tokens, int32_t* slots, int32_t* cow_pair,
                                  int32_t* num_cow);
+
+/* One decode step: token tokens[i] appended to sequence seq_ids[i] for
+ * i = 0 .. num_seqs-1, in that order (each id at most once).  Writes slots
+ * [num_seqs] and the step's copy-on-write pairs, in order, to
+ * cow_pairs[num_seqs, 2] with their count in *num_cow.  The exact block demand
+ * of the whole step is checked first: PKV_EWORKSPACE leaves every sequence as
+ * it was. */
+PKV_API pkv_status pkv_bm_append_step(pkv_block_manager* bm, const int64_t* seq_ids,
+                                      int32_t num_seqs, const int32_t* tokens, int32_t* slots,
+                                      int32_t* cow_pairs, int32_t* num_cow);
+
+/* Swap a sequence out of the pool when it runs short ("The Memory Wall", "The
+ * Infrastructure Impact: Scale and Complexity", item "The Block Manager"; "05
+ * PagedAttention", "Managing Virtual Memory (Block Manager)"): writes its block
+ * table to block_ids[capacity] (*num_ids entries, table order: the blocks to
+ * pass to paged_swap_out before anything reuses them) and releases them.  The
+ * sequence keeps its tokens; until pkv_bm_swap_in it can only be freed. */
+PKV_API pkv_status pkv_bm_swap_out(pkv_block_manager* bm, int64_t seq_id, int32_t* block_ids,
+                                   int32_t capacity, int32_t* num_ids);
+/* Bring a swapped-out sequence back: takes ceil(tokens / block_size) blocks
+ * like any allocation and writes them to block_ids (table order: the
+ * destinations to pass to paged_swap_in with the host image).  PKV_EWORKSPACE,
+ * nothing changed, when the pool cannot hold it. */
+PKV_API pkv_status pkv_bm_swap_in(pkv_block_manager* bm, int64_t seq_id, int32_t* block_ids,
+                                  int32_t capacity, int32_t* num_ids);
 
 /* child shares all of parent's blocks (parallel sampling, beam search). */
 PKV_API pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);

@@ -25,4 +25,6 @@ from .paged_attention import (  # noqa: F401
     partition_states,
     split_decode_attention,
     storage_to_f64,
+    swap_in,
+    swap_out,
 )

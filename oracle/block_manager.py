@@ -40,8 +40,20 @@ Readings (the pages fix none of these):
   -1 for every reused token;
 * appending to a sequence whose last block is partly filled and shared first
   copies that block (one copy-on-write pair), then writes into the copy;
-* an add or append the pool cannot hold fails before changing anything.
+* an add or append the pool cannot hold fails before changing anything;
+* a decode step appends one token to each listed sequence, in list order, and
+  fails before changing anything unless the pool holds the whole step;
+* swapping a sequence out (its blocks go to CPU RAM: "The Memory Wall", "The
+  Infrastructure Impact: Scale and Complexity", item "The Block Manager"; "05
+  PagedAttention", "Managing Virtual Memory (Block Manager)") returns its
+  block table, the blocks to copy out in order, and releases them last block
+  first; the sequence keeps its tokens.  Swapping it back in takes
+  ceil(n / block_size) blocks the way any allocation does and offers its full
+  blocks to the cache again.  A swapped-out sequence can only be swapped in
+  or freed.
 """
+
+import copy
 
 
 class BlockManagerModel:
@@ -170,10 +182,16 @@ class BlockManagerModel:
         self._register_full_blocks(seq)
         return slots, cow
 
+    def _live(self, seq_id):
+        seq = self.seqs[seq_id]
+        if seq.get("swapped"):
+            raise KeyError("sequence is swapped out")
+        return seq
+
     def append(self, seq_id, tokens):
         """Append new tokens.  Returns (slots, copy-on-write pair or None).
         Raises MemoryError, changing nothing, when the pool cannot hold them."""
-        seq = self.seqs[seq_id]
+        seq = self._live(seq_id)
         tokens = list(tokens)
         if self.num_free() < self._needed(seq, len(tokens)):
             raise MemoryError("no free block")
@@ -182,7 +200,7 @@ class BlockManagerModel:
     def fork(self, parent, child):
         if child in self.seqs:
             raise KeyError("sequence exists")
-        p = self.seqs[parent]
+        p = self._live(parent)
         for b in p["blocks"]:
             self._reuse(b)
         self.seqs[child] = {"blocks": list(p["blocks"]), "tokens": list(p["tokens"]),
@@ -193,8 +211,55 @@ class BlockManagerModel:
         for b in reversed(seq["blocks"]):
             self._release(b)
 
+    def append_step(self, seq_ids, tokens):
+        """One decode step: token tokens[i] appended to sequence seq_ids[i], in
+        order.  Returns (slots, copy-on-write pairs in order).  If the pool
+        cannot hold the whole step, raises MemoryError with nothing changed
+        (the step is tried on a copy of the state first)."""
+        if len(set(seq_ids)) != len(seq_ids):
+            raise KeyError("sequence listed twice")
+        for sid in seq_ids:
+            self._live(sid)
+        trial = copy.deepcopy(self)
+        for sid, t in zip(seq_ids, tokens):
+            trial.append(sid, [t])            # raises MemoryError on exhaustion
+        slots, cows = [], []
+        for sid, t in zip(seq_ids, tokens):
+            sl, cow = self.append(sid, [t])
+            slots += sl
+            if cow is not None:
+                cows.append(cow)
+        return slots, cows
+
+    def swap_out(self, seq_id):
+        """Release a sequence's blocks (last first); returns them in table
+        order, the blocks whose contents go to host memory."""
+        seq = self._live(seq_id)
+        blocks = list(seq["blocks"])
+        for b in reversed(blocks):
+            self._release(b)
+        seq["blocks"] = []
+        seq["swapped"] = True
+        return blocks
+
+    def swap_in(self, seq_id):
+        """Give a swapped-out sequence fresh blocks; returns them in table
+        order, the blocks its host copy goes back into.  Raises MemoryError,
+        changing nothing, when the pool cannot hold it."""
+        seq = self.seqs[seq_id]
+        if not seq.get("swapped"):
+            raise KeyError("sequence is not swapped out")
+        need = -(-len(seq["tokens"]) // self.bs)
+        if self.num_free() < need:
+            raise MemoryError("no free block")
+        seq["blocks"] = [self._take() for _ in range(need)]
+        seq["swapped"] = False
+        seq["keyed"] = 0
+        self._register_full_blocks(seq)
+        return list(seq["blocks"])
+
     def block_table(self, seq_id):
-        return list(self.seqs[seq_id]["blocks"])
+        return list(self._live(seq_id)["blocks"])
 
     def num_tokens(self, seq_id):
         return len(self.seqs[seq_id]["tokens"])

@@ -24,6 +24,10 @@ What is computed, and where the pages state it
 * Copy-on-write gives a writer its own copy of a shared block while the shared
   block stays unchanged ("05 PagedAttention", section "KV Cache Sharing
   (Copy-on-Write)"; first page, section "Copy-on-Write"): ``copy_blocks``.
+* Blocks can be moved to CPU RAM and back when the pool runs short ("The
+  Memory Wall", "The Infrastructure Impact: Scale and Complexity"; "05
+  PagedAttention", "Managing Virtual Memory (Block Manager)"): ``swap_out`` and
+  ``swap_in``.
 
 Readings where the pages are silent:
 * pool layout ``[num_blocks, H_kv, block_size, D]`` for K and V alike;
@@ -32,6 +36,8 @@ Readings where the pages are silent:
   appended in the same step included;
 * ``slot = physical_block * block_size + offset``; a negative slot is skipped;
 * a sequence with zero context yields a zero output row;
+* a swapped-out batch of blocks is one contiguous host image, entry i holding
+  the i-th listed block's K tile then its V tile;
 * storage types are fp32, fp16 and bf16; fp16/bf16 arrays are passed as their
   raw 16-bit patterns (``uint16``) and decoded exactly to fp64.
 """
@@ -327,4 +333,50 @@ def copy_blocks(k_cache, v_cache, block_mapping):
     for src, dst in pairs:
         kc[dst] = k0[src]
         vc[dst] = v0[src]
+    return kc.view(np.asarray(k_cache).dtype), vc.view(np.asarray(v_cache).dtype)
+
+
+# ---------------------------------------------------------------------------
+# swap to host memory and back (bit copies)
+# ---------------------------------------------------------------------------
+#
+# When the pool runs short the block manager may move a sequence's blocks out
+# to CPU RAM and bring them back later ("The Memory Wall", "The Infrastructure
+# Impact: Scale and Complexity", item "The Block Manager"; "05 PagedAttention",
+# "Managing Virtual Memory (Block Manager)", its eviction entry).  The pages
+# fix no host layout.  Reading taken: a swap moves an ordered list of block ids
+# into one contiguous host image, entry i holding block ids[i]'s K tile and
+# then its V tile ([n, 2, H_kv, bs, D]); bringing it back writes entry i into
+# block ids[i] of the pools, which need not be the block it came from.
+
+def swap_out(k_cache, v_cache, block_ids):
+    """Host image [n, 2, H_kv, bs, D] of the listed blocks, raw bits.  An id
+    outside the pool gives an all-zero entry."""
+    kc = _bits(k_cache)
+    vc = _bits(v_cache)
+    nb = kc.shape[0]
+    image = np.zeros((len(block_ids), 2) + kc.shape[1:], dtype=kc.dtype)
+    for i, b in enumerate(block_ids):
+        b = int(b)
+        if 0 <= b < nb:
+            image[i, 0] = kc[b]
+            image[i, 1] = vc[b]
+    return image.view(np.asarray(k_cache).dtype)
+
+
+def swap_in(k_cache, v_cache, image, block_ids):
+    """Write entry i of a host image into block block_ids[i] of both pools.
+    Destinations must be distinct; an id outside the pool is skipped.  Returns
+    new pools; the inputs are not modified."""
+    ids = [int(b) for b in block_ids]
+    inside = [b for b in ids if 0 <= b < np.asarray(k_cache).shape[0]]
+    if len(set(inside)) != len(inside):
+        raise ValueError("swap_in: duplicate destination block")
+    kc = _bits(k_cache).copy()
+    vc = _bits(v_cache).copy()
+    img = _bits(image)
+    for i, b in enumerate(ids):
+        if 0 <= b < kc.shape[0]:
+            kc[b] = img[i, 0]
+            vc[b] = img[i, 1]
     return kc.view(np.asarray(k_cache).dtype), vc.view(np.asarray(v_cache).dtype)

@@ -15,6 +15,8 @@ from ._lib import (  # noqa: F401
     paged_attention_workspace_bytes,
     paged_copy_blocks,
     paged_kv_append,
+    paged_swap_in,
+    paged_swap_out,
     partition_tokens,
     pkv_stream_copy,
 )

@@ -60,6 +60,10 @@ def load():
     lib.paged_attention_multi.restype = c_i32
     lib.paged_copy_blocks.argtypes = [c_vp, c_vp, PkvPool, c_vp, c_i32, c_vp]
     lib.paged_copy_blocks.restype = c_i32
+    lib.paged_swap_out.argtypes = [c_vp, c_vp, PkvPool, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]
+    lib.paged_swap_out.restype = c_i32
+    lib.paged_swap_in.argtypes = [c_vp, c_i32, c_vp, c_vp, PkvPool, c_vp, c_vp, c_sz, c_vp]
+    lib.paged_swap_in.restype = c_i32
     lib.pkv_stream_copy.argtypes = [c_vp, c_vp, c_sz, c_vp]
     lib.pkv_stream_copy.restype = c_i32
     lib.pkv_stream_read.argtypes = [c_vp, c_sz, c_vp, c_vp]
@@ -223,6 +227,54 @@ def paged_copy_blocks(k_cache, v_cache, block_mapping, stream=None):
                                     block_mapping.shape[0], _stream(stream)))
 
 
+SWAP_STAGING_BYTES = 64 << 20
+
+
+def _swap_args(k_cache, v_cache, block_ids, staging):
+    pool = _pools(k_cache, v_cache)
+    _need(block_ids, "block_ids", dtype=torch.int32, dim=1, device=k_cache.device)
+    entry = 2 * k_cache[0].numel() * k_cache.element_size()
+    n = block_ids.shape[0]
+    if staging is None:
+        nbytes = min(max(n, 1) * entry, max(entry, SWAP_STAGING_BYTES // entry * entry))
+        staging = torch.empty(nbytes, dtype=torch.uint8, device=k_cache.device)
+    else:
+        _need(staging, "staging", device=k_cache.device)
+    return pool, n, (n, 2) + tuple(k_cache.shape[1:]), staging
+
+
+def _need_host(t, name, dtype, shape):
+    if not isinstance(t, torch.Tensor) or t.is_cuda:
+        raise ValueError(f"{name} must be a host tensor")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+
+
+def paged_swap_out(k_cache, v_cache, block_ids, host_image=None, staging=None, stream=None):
+    """Copy the listed blocks to a host image [n, 2, H_kv, bs, D] (entry i:
+    block_ids[i]'s K then V).  Allocates a pinned image when none is given.
+    Asynchronous: the image is complete once the stream is synchronized."""
+    pool, n, shape, staging = _swap_args(k_cache, v_cache, block_ids, staging)
+    if host_image is None:
+        host_image = torch.empty(shape, dtype=k_cache.dtype, pin_memory=True)
+    _need_host(host_image, "host_image", k_cache.dtype, shape)
+    _check(load().paged_swap_out(_ptr(k_cache), _ptr(v_cache), pool, _ptr(block_ids), n,
+                                 _ptr(host_image), _ptr(staging),
+                                 staging.numel() * staging.element_size(), _stream(stream)))
+    return host_image
+
+
+def paged_swap_in(host_image, k_cache, v_cache, block_ids, staging=None, stream=None):
+    """Write entry i of a host image into block block_ids[i] of both pools
+    (distinct destinations).  The host image must stay untouched until the
+    stream has reached the end of the call."""
+    pool, n, shape, staging = _swap_args(k_cache, v_cache, block_ids, staging)
+    _need_host(host_image, "host_image", k_cache.dtype, shape)
+    _check(load().paged_swap_in(_ptr(host_image), n, _ptr(k_cache), _ptr(v_cache), pool,
+                                _ptr(block_ids), _ptr(staging),
+                                staging.numel() * staging.element_size(), _stream(stream)))
+
+
 def pkv_stream_copy(dst, src, stream=None):
     """Plain 16-byte-vector device copy of src into dst (same byte size)."""
     _need(dst, "dst")
@@ -274,6 +326,12 @@ def _bm_lib():
     lib.pkv_bm_add_sequence.restype = c_i32
     lib.pkv_bm_append.argtypes = [c_vp, c_i64, c_vp, c_i32, c_vp, c_vp, c_vp]
     lib.pkv_bm_append.restype = c_i32
+    lib.pkv_bm_append_step.argtypes = [c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp]
+    lib.pkv_bm_append_step.restype = c_i32
+    lib.pkv_bm_swap_out.argtypes = [c_vp, c_i64, c_vp, c_i32, c_vp]
+    lib.pkv_bm_swap_out.restype = c_i32
+    lib.pkv_bm_swap_in.argtypes = [c_vp, c_i64, c_vp, c_i32, c_vp]
+    lib.pkv_bm_swap_in.restype = c_i32
     lib.pkv_bm_fork.argtypes = [c_vp, c_i64, c_i64]
     lib.pkv_bm_fork.restype = c_i32
     lib.pkv_bm_free_sequence.argtypes = [c_vp, c_i64]
@@ -343,6 +401,39 @@ class BlockManager:
         self._ok(self._lib.pkv_bm_append(self._h, int(seq_id), t.ctypes.data, len(t),
                                          slots.ctypes.data, cow.ctypes.data, ctypes.byref(ncow)))
         return slots, ((int(cow[0]), int(cow[1])) if ncow.value else None)
+
+    def append_step(self, seq_ids, tokens):
+        """One token per listed sequence.  Returns (slots [B] int32,
+        copy-on-write pairs [k, 2] int32 in order)."""
+        ids = self._np.ascontiguousarray(seq_ids, dtype=self._np.int64)
+        t = self._i32(tokens)
+        if len(t) != len(ids):
+            raise ValueError("one token per sequence")
+        slots = self._np.empty(len(ids), dtype=self._np.int32)
+        cows = self._np.empty((len(ids), 2), dtype=self._np.int32)
+        ncow = ctypes.c_int32(0)
+        self._ok(self._lib.pkv_bm_append_step(self._h, ids.ctypes.data, len(ids), t.ctypes.data,
+                                              slots.ctypes.data, cows.ctypes.data,
+                                              ctypes.byref(ncow)))
+        return slots, cows[:ncow.value]
+
+    def _swap(self, fn, seq_id):
+        n, _ = self.sequence_info(seq_id)
+        cap = -(-n // self.block_size)
+        ids = self._np.empty(max(cap, 1), dtype=self._np.int32)
+        got = ctypes.c_int32(0)
+        self._ok(fn(self._h, int(seq_id), ids.ctypes.data, cap, ctypes.byref(got)))
+        return ids[:got.value]
+
+    def swap_out(self, seq_id):
+        """Release the sequence's blocks; returns them (int32, table order),
+        the blocks to copy to host memory before anything reuses them."""
+        return self._swap(self._lib.pkv_bm_swap_out, seq_id)
+
+    def swap_in(self, seq_id):
+        """Fresh blocks for a swapped-out sequence (int32, table order), the
+        destinations of its host copy."""
+        return self._swap(self._lib.pkv_bm_swap_in, seq_id)
 
     def fork(self, parent, child):
         self._ok(self._lib.pkv_bm_fork(self._h, int(parent), int(child)))

@@ -23,7 +23,12 @@
 //    tokens);
 //  - a new sequence reuses its longest run of cached leading full blocks, but
 //    never the block holding its last prompt token;
-//  - an add or append the pool cannot hold fails before changing anything.
+//  - an add or append the pool cannot hold fails before changing anything;
+//  - a sequence swapped out to host memory releases all its blocks and keeps
+//    its tokens; brought back, it takes fresh blocks like any allocation
+//    ("The Memory Wall", "The Infrastructure Impact: Scale and Complexity",
+//    item "The Block Manager"; "05 PagedAttention", "Managing Virtual Memory
+//    (Block Manager)").
 // Not thread-safe: one manager is driven by one thread at a time.
 
 #include <stdint.h>
@@ -83,6 +88,7 @@ struct Sequence {
   std::vector<int32_t> tokens;  // every token id (needed to key its full blocks)
   Key tail_key = kRootKey;      // key of the prefix ending at its last cached-or-keyed full block
   int32_t keyed_blocks = 0;     // leading full blocks whose keys are folded into tail_key
+  bool swapped = false;         // blocks moved to host memory; none held in the pool
 };
 
 }  // namespace
@@ -271,6 +277,7 @@ pkv_status pkv_bm_append(pkv_block_manager* bm, int64_t seq_id, const int32_t* t
   if (!bm || num_tokens < 0 || (num_tokens > 0 && !tokens)) return bm_fail(PKV_EINVAL, "bad argument");
   auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return bm_fail(PKV_EINVAL, "unknown sequence id");
+  if (it->second.swapped) return bm_fail(PKV_EINVAL, "sequence is swapped out");
   if (num_cow) *num_cow = 0;
   if (bm->num_free() < bm->needed(it->second, num_tokens))
     return bm_fail(PKV_EWORKSPACE, "block pool exhausted");
@@ -288,6 +295,7 @@ pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child) {
   auto it = bm->seqs.find(parent);
   if (it == bm->seqs.end()) return bm_fail(PKV_EINVAL, "unknown sequence id");
   if (bm->seqs.count(child)) return bm_fail(PKV_EINVAL, "sequence id already in use");
+  if (it->second.swapped) return bm_fail(PKV_EINVAL, "sequence is swapped out");
   try {
     Sequence copy = it->second;
     for (int32_t b : copy.blocks) bm->reuse(b);
@@ -306,6 +314,104 @@ pkv_status pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq_id) {
   const std::vector<int32_t>& blocks = it->second.blocks;
   for (size_t j = blocks.size(); j-- > 0;) bm->release(blocks[j]);
   bm->seqs.erase(it);
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_append_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t num_seqs,
+                              const int32_t* tokens, int32_t* slots, int32_t* cow_pairs,
+                              int32_t* num_cow) {
+  g_bm_err[0] = '\0';
+  if (!bm || num_seqs < 0 || (num_seqs > 0 && (!seq_ids || !tokens || !slots || !cow_pairs)) ||
+      !num_cow)
+    return bm_fail(PKV_EINVAL, "bad argument");
+  *num_cow = 0;
+  try {
+    std::vector<Sequence*> seqs((size_t)num_seqs);
+    std::unordered_map<int32_t, int32_t> shared_left;  // last block -> references left to copy away
+    int64_t need = 0;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      auto it = bm->seqs.find(seq_ids[i]);
+      if (it == bm->seqs.end()) return bm_fail(PKV_EINVAL, "unknown sequence id");
+      if (it->second.swapped) return bm_fail(PKV_EINVAL, "sequence is swapped out");
+      seqs[(size_t)i] = &it->second;
+    }
+    {
+      std::unordered_map<const Sequence*, int32_t> seen;
+      for (int32_t i = 0; i < num_seqs; ++i)
+        if (seen[seqs[(size_t)i]]++) return bm_fail(PKV_EINVAL, "sequence listed twice");
+    }
+    // Exact block demand of the whole step, in order: a full last block needs
+    // a new one; a shared partly filled one needs a copy, unless every other
+    // holder of it has already copied it away earlier in this step.
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      const Sequence& q = *seqs[(size_t)i];
+      if (q.tokens.size() % (size_t)bm->block_size == 0) {
+        ++need;
+        continue;
+      }
+      const int32_t last = q.blocks.back();
+      auto f = shared_left.find(last);
+      const int32_t refs = f == shared_left.end() ? bm->ref[last] : f->second;
+      if (refs > 1) {
+        ++need;
+        shared_left[last] = refs - 1;
+      }
+    }
+    if (need > bm->num_free()) return bm_fail(PKV_EWORKSPACE, "block pool exhausted");
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      int32_t one = 0;
+      bm->append(*seqs[(size_t)i], tokens + i, 1, slots + i, cow_pairs + 2 * (size_t)*num_cow, &one);
+      *num_cow += one;
+    }
+  } catch (...) {
+    return bm_fail(PKV_EINVAL, "out of host memory");
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_swap_out(pkv_block_manager* bm, int64_t seq_id, int32_t* block_ids,
+                           int32_t capacity, int32_t* num_ids) {
+  g_bm_err[0] = '\0';
+  if (!bm || !num_ids || capacity < 0 || (capacity > 0 && !block_ids))
+    return bm_fail(PKV_EINVAL, "bad argument");
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return bm_fail(PKV_EINVAL, "unknown sequence id");
+  Sequence& s = it->second;
+  if (s.swapped) return bm_fail(PKV_EINVAL, "sequence is swapped out");
+  if ((int64_t)s.blocks.size() > capacity) return bm_fail(PKV_EINVAL, "block_ids too short");
+  *num_ids = (int32_t)s.blocks.size();
+  for (size_t j = 0; j < s.blocks.size(); ++j) block_ids[j] = s.blocks[j];
+  for (size_t j = s.blocks.size(); j-- > 0;) bm->release(s.blocks[j]);
+  s.blocks.clear();
+  s.swapped = true;
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_swap_in(pkv_block_manager* bm, int64_t seq_id, int32_t* block_ids,
+                          int32_t capacity, int32_t* num_ids) {
+  g_bm_err[0] = '\0';
+  if (!bm || !num_ids || capacity < 0 || (capacity > 0 && !block_ids))
+    return bm_fail(PKV_EINVAL, "bad argument");
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return bm_fail(PKV_EINVAL, "unknown sequence id");
+  Sequence& s = it->second;
+  if (!s.swapped) return bm_fail(PKV_EINVAL, "sequence is not swapped out");
+  const int64_t bs = bm->block_size;
+  const int32_t need = (int32_t)(((int64_t)s.tokens.size() + bs - 1) / bs);
+  if (need > capacity) return bm_fail(PKV_EINVAL, "block_ids too short");
+  if (need > bm->num_free()) return bm_fail(PKV_EWORKSPACE, "block pool exhausted");
+  try {
+    s.blocks.reserve((size_t)need);
+    for (int32_t j = 0; j < need; ++j) s.blocks.push_back(bm->take());
+    s.swapped = false;
+    s.tail_key = kRootKey;
+    s.keyed_blocks = 0;
+    bm->register_full(s);
+  } catch (...) {
+    return bm_fail(PKV_EINVAL, "out of host memory");
+  }
+  *num_ids = need;
+  for (int32_t j = 0; j < need; ++j) block_ids[j] = s.blocks[(size_t)j];
   return PKV_OK;
 }
 
@@ -329,6 +435,7 @@ pkv_status pkv_bm_build_batch(const pkv_block_manager* bm, const int64_t* seq_id
   for (int32_t i = 0; i < num_seqs; ++i) {
     auto it = bm->seqs.find(seq_ids[i]);
     if (it == bm->seqs.end()) return bm_fail(PKV_EINVAL, "unknown sequence id");
+    if (it->second.swapped) return bm_fail(PKV_EINVAL, "sequence is swapped out");
     if ((int64_t)it->second.blocks.size() > max_blocks_per_seq)
       return bm_fail(PKV_EINVAL, "a sequence has more blocks than max_blocks_per_seq");
   }

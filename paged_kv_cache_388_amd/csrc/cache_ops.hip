@@ -9,6 +9,12 @@
 // Copy: a writer to a shared block first gets a private copy while the shared
 // block stays unchanged ("05 PagedAttention", "KV Cache Sharing
 // (Copy-on-Write)"; first page, "Copy-on-Write").
+// Swap: when the pool runs short, blocks move to CPU RAM and come back later
+// ("The Memory Wall", "The Infrastructure Impact: Scale and Complexity", item
+// "The Block Manager"; "05 PagedAttention", "Managing Virtual Memory (Block
+// Manager)").  A gather packs the listed blocks into a contiguous device
+// staging run so that one DMA copy moves the run over PCIe; a scatter unpacks
+// a run copied back.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -56,6 +62,38 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
   const uint4* from = reinterpret_cast<const uint4*>(pool + (int64_t)src * block_chunks * 16);
   uint4* to = reinterpret_cast<uint4*>(pool + (int64_t)dst * block_chunks * 16);
   for (int64_t c = threadIdx.x; c < block_chunks; c += kThreads) to[c] = from[c];
+}
+
+// Swap gather: workgroup (i, K or V) copies block ids[i]'s tile of every KV
+// head into staging entry 2i (K) or 2i+1 (V).  An id outside the pool gives a
+// zero entry.  Both sides are contiguous runs of tile_chunks 16-byte chunks.
+__global__ __launch_bounds__(kThreads) void swap_gather_kernel(
+    const char* __restrict__ k_cache, const char* __restrict__ v_cache,
+    const int32_t* __restrict__ ids, uint4* __restrict__ staging, int64_t tile_chunks,
+    int32_t num_blocks) {
+  const int i = blockIdx.x >> 1;
+  const char* pool = (blockIdx.x & 1) ? v_cache : k_cache;
+  const int32_t b = ids[i];
+  uint4* to = staging + (int64_t)blockIdx.x * tile_chunks;
+  if ((unsigned)b >= (unsigned)num_blocks) {
+    for (int64_t c = threadIdx.x; c < tile_chunks; c += kThreads) to[c] = make_uint4(0, 0, 0, 0);
+    return;
+  }
+  const uint4* from = reinterpret_cast<const uint4*>(pool + (int64_t)b * tile_chunks * 16);
+  for (int64_t c = threadIdx.x; c < tile_chunks; c += kThreads) to[c] = from[c];
+}
+
+// Swap scatter: the reverse; an id outside the pool is skipped.
+__global__ __launch_bounds__(kThreads) void swap_scatter_kernel(
+    char* __restrict__ k_cache, char* __restrict__ v_cache, const int32_t* __restrict__ ids,
+    const uint4* __restrict__ staging, int64_t tile_chunks, int32_t num_blocks) {
+  const int i = blockIdx.x >> 1;
+  char* pool = (blockIdx.x & 1) ? v_cache : k_cache;
+  const int32_t b = ids[i];
+  if ((unsigned)b >= (unsigned)num_blocks) return;
+  const uint4* from = staging + (int64_t)blockIdx.x * tile_chunks;
+  uint4* to = reinterpret_cast<uint4*>(pool + (int64_t)b * tile_chunks * 16);
+  for (int64_t c = threadIdx.x; c < tile_chunks; c += kThreads) to[c] = from[c];
 }
 
 __global__ __launch_bounds__(kThreads) void stream_copy_kernel(uint4* __restrict__ dst,
@@ -122,6 +160,26 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block
   hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs * 2u), dim3(kThreads), 0, stream,
                      static_cast<char*>(k_cache), static_cast<char*>(v_cache), block_mapping,
                      (int64_t)(block_bytes / 16), num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_gather(const void* k_cache, const void* v_cache, const int32_t* ids,
+                              int32_t count, void* staging, size_t block_bytes, int32_t num_blocks,
+                              hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(swap_gather_kernel, dim3((unsigned)count * 2u), dim3(kThreads), 0, stream,
+                     static_cast<const char*>(k_cache), static_cast<const char*>(v_cache), ids,
+                     static_cast<uint4*>(staging), (int64_t)(block_bytes / 16), num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_scatter(void* k_cache, void* v_cache, const int32_t* ids, int32_t count,
+                               const void* staging, size_t block_bytes, int32_t num_blocks,
+                               hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(swap_scatter_kernel, dim3((unsigned)count * 2u), dim3(kThreads), 0, stream,
+                     static_cast<char*>(k_cache), static_cast<char*>(v_cache), ids,
+                     static_cast<const uint4*>(staging), (int64_t)(block_bytes / 16), num_blocks);
   return hipGetLastError();
 }
 

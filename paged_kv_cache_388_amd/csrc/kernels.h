@@ -88,6 +88,14 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block
                               int32_t num_pairs, size_t block_bytes, int32_t num_blocks,
                               hipStream_t stream);
 
+// Swap staging: entry 2i / 2i+1 of `staging` is block ids[i]'s K / V tile
+// (block_bytes each, every KV head).
+hipError_t launch_swap_gather(const void* k_cache, const void* v_cache, const int32_t* ids,
+                              int32_t count, void* staging, size_t block_bytes, int32_t num_blocks,
+                              hipStream_t stream);
+hipError_t launch_swap_scatter(void* k_cache, void* v_cache, const int32_t* ids, int32_t count,
+                               const void* staging, size_t block_bytes, int32_t num_blocks,
+                               hipStream_t stream);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
 // sink: kStreamReadWorkgroups uint32 words, one per workgroup.

@@ -298,6 +298,75 @@ pkv_status paged_copy_blocks(void* k_cache, void* v_cache, pkv_pool pool,
   return err == hipSuccess ? PKV_OK : hip_fail(err, "paged_copy_blocks launch");
 }
 
+namespace {
+
+// Shared checks of the two swap directions; *per_run = blocks per staging run.
+pkv_status swap_check(const char* what, const void* k_cache, const void* v_cache,
+                      const pkv_pool& pool, const int32_t* block_ids, int32_t num_ids,
+                      const void* host_image, const void* staging, size_t staging_bytes,
+                      int32_t* per_run) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (num_ids < 0) return fail(PKV_EINVAL, "%s: num_ids %d < 0", what, num_ids);
+  if (num_ids == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !block_ids || !host_image || !staging)
+    return fail(PKV_EINVAL, "%s: null pointer argument", what);
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(staging))
+    return fail(PKV_EINVAL, "%s: pools and staging must be 16-byte aligned", what);
+  const size_t entry = 2 * pool_block_bytes(pool);
+  if (staging_bytes < entry)
+    return fail(PKV_EWORKSPACE, "%s: staging holds %zu bytes, one block needs %zu", what,
+                staging_bytes, entry);
+  const size_t run = staging_bytes / entry;
+  *per_run = run > 0x3fffffff ? 0x3fffffff : (int32_t)run;
+  return PKV_OK;
+}
+
+}  // namespace
+
+pkv_status paged_swap_out(const void* k_cache, const void* v_cache, pkv_pool pool,
+                          const int32_t* block_ids, int32_t num_ids, void* host_image,
+                          void* staging, size_t staging_bytes, hipStream_t stream) {
+  g_err[0] = '\0';
+  int32_t per_run = 0;
+  pkv_status st = swap_check("paged_swap_out", k_cache, v_cache, pool, block_ids, num_ids,
+                             host_image, staging, staging_bytes, &per_run);
+  if (st != PKV_OK || num_ids == 0) return st;
+  const size_t bb = pool_block_bytes(pool);
+  for (int32_t start = 0; start < num_ids; start += per_run) {
+    const int32_t cnt = num_ids - start < per_run ? num_ids - start : per_run;
+    hipError_t err = pkv::launch_swap_gather(k_cache, v_cache, block_ids + start, cnt, staging, bb,
+                                             pool.num_blocks, stream);
+    if (err != hipSuccess) return hip_fail(err, "paged_swap_out gather launch");
+    err = hipMemcpyAsync(static_cast<char*>(host_image) + (size_t)start * 2 * bb, staging,
+                         (size_t)cnt * 2 * bb, hipMemcpyDeviceToHost, stream);
+    if (err != hipSuccess) return hip_fail(err, "paged_swap_out copy to host");
+  }
+  return PKV_OK;
+}
+
+pkv_status paged_swap_in(const void* host_image, int32_t num_ids, void* k_cache, void* v_cache,
+                         pkv_pool pool, const int32_t* block_ids, void* staging,
+                         size_t staging_bytes, hipStream_t stream) {
+  g_err[0] = '\0';
+  int32_t per_run = 0;
+  pkv_status st = swap_check("paged_swap_in", k_cache, v_cache, pool, block_ids, num_ids,
+                             host_image, staging, staging_bytes, &per_run);
+  if (st != PKV_OK || num_ids == 0) return st;
+  const size_t bb = pool_block_bytes(pool);
+  for (int32_t start = 0; start < num_ids; start += per_run) {
+    const int32_t cnt = num_ids - start < per_run ? num_ids - start : per_run;
+    hipError_t err = hipMemcpyAsync(staging,
+                                    static_cast<const char*>(host_image) + (size_t)start * 2 * bb,
+                                    (size_t)cnt * 2 * bb, hipMemcpyHostToDevice, stream);
+    if (err != hipSuccess) return hip_fail(err, "paged_swap_in copy from host");
+    err = pkv::launch_swap_scatter(k_cache, v_cache, block_ids + start, cnt, staging, bb,
+                                   pool.num_blocks, stream);
+    if (err != hipSuccess) return hip_fail(err, "paged_swap_in scatter launch");
+  }
+  return PKV_OK;
+}
+
 pkv_status pkv_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
   g_err[0] = '\0';
   if (bytes == 0) return PKV_OK;

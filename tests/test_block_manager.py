@@ -128,26 +128,40 @@ def _trace(seed, ops, num_blocks, block_size, prefix_cache):
     rng = np.random.default_rng(seed)
     prompts = [list(rng.integers(0, 50, size=int(rng.integers(1, 6 * block_size))))
                for _ in range(4)]
-    live = []
+    live, out = [], []
     next_id = 0
     for _ in range(ops):
         r = rng.random()
-        if r < 0.30 or not live:
+        if r < 0.22 or not live:
             base = prompts[int(rng.integers(0, len(prompts)))] if rng.random() < 0.7 else []
             tail = list(rng.integers(0, 50, size=int(rng.integers(1, 3 * block_size))))
             yield ("add", next_id, base + tail)
             live.append(next_id)
             next_id += 1
-        elif r < 0.70:
+        elif r < 0.50:
             sid = live[int(rng.integers(0, len(live)))]
             yield ("append", sid, list(rng.integers(0, 50, size=int(rng.integers(1, 2 * block_size)))))
-        elif r < 0.82:
+        elif r < 0.62:
+            k = int(rng.integers(1, len(live) + 1))
+            ids = [int(x) for x in rng.choice(live, size=k, replace=False)]
+            yield ("step", ids, [int(x) for x in rng.integers(0, 50, size=k)])
+        elif r < 0.72:
             sid = live[int(rng.integers(0, len(live)))]
             yield ("fork", sid, next_id)
             live.append(next_id)
             next_id += 1
-        else:
+        elif r < 0.80:
             sid = live.pop(int(rng.integers(0, len(live))))
+            out.append(sid)
+            yield ("swap_out", sid, None)
+        elif r < 0.88 and out:
+            sid = out.pop(int(rng.integers(0, len(out))))
+            live.append(sid)
+            yield ("swap_in", sid, None)
+        else:
+            pool = live + out
+            sid = pool[int(rng.integers(0, len(pool)))]
+            (live if sid in live else out).remove(sid)
             yield ("free", sid, None)
 
 
@@ -157,12 +171,25 @@ def _same_state(cpp, model, live, max_blocks):
     ref = model.stats()
     for k in ("blocks_in_use", "tokens_stored", "slots_reserved", "cached_blocks"):
         assert st[k] == ref[k], k
+    assert st["num_sequences"] == len(model.seqs)
     if live:
         bt, lens = cpp.build_batch(live, max_blocks)
         for i, sid in enumerate(live):
             table = model.block_table(sid)
             assert list(bt[i, :len(table)]) == table and np.all(bt[i, len(table):] == -1)
             assert lens[i] == model.num_tokens(sid)
+
+
+def _both(cpp_call, model_call):
+    """Run one operation on both managers: same result, or both exhausted."""
+    try:
+        want = model_call()
+    except MemoryError:
+        with pytest.raises(_lib.PagedKVError) as e:
+            cpp_call()
+        assert e.value.status == 3
+        return None, True
+    return (cpp_call(), want), False
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -172,47 +199,98 @@ def test_cpp_manager_matches_model(seed, prefix_cache):
     nb = [24, 40, 200][seed % 3]
     cpp = _lib.BlockManager(nb, bs, prefix_cache=prefix_cache)
     model = obm.BlockManagerModel(nb, bs, prefix_cache=prefix_cache)
-    live = []
-    exhausted = 0
+    live, out = [], []
+    exhausted = swaps = steps = 0
     for op, a, b in _trace(1000 + seed, 400, nb, bs, prefix_cache):
+        known = a in live if op in ("append", "fork", "swap_out") else True
+        if op == "step":
+            a = [x for x in a if x in live]
+            b = b[:len(a)]
+        if op == "swap_in" and a not in out:
+            continue
+        if op == "free" and a not in live and a not in out:
+            continue
+        if not known:
+            continue
         if op == "add":
-            try:
-                want = model.add_sequence(a, b)
-            except MemoryError:
-                with pytest.raises(_lib.PagedKVError) as e:
-                    cpp.add_sequence(a, b)
-                assert e.value.status == 3
-                exhausted += 1
-                continue
-            reused, slots = cpp.add_sequence(a, b)
-            assert (reused, list(slots)) == (want[0], list(want[1]))
-            live.append(a)
+            got, full = _both(lambda: cpp.add_sequence(a, b), lambda: model.add_sequence(a, b))
+            if not full:
+                (reused, slots), want = got
+                assert (reused, list(slots)) == (want[0], list(want[1]))
+                live.append(a)
         elif op == "append":
-            if a not in live:
-                continue
-            try:
-                want_slots, want_cow = model.append(a, b)
-            except MemoryError:
-                with pytest.raises(_lib.PagedKVError):
-                    cpp.append(a, b)
-                exhausted += 1
-                continue
-            slots, cow = cpp.append(a, b)
-            assert list(slots) == want_slots and cow == want_cow
+            got, full = _both(lambda: cpp.append(a, b), lambda: model.append(a, b))
+            if not full:
+                (slots, cow), (want_slots, want_cow) = got
+                assert list(slots) == want_slots and cow == want_cow
+        elif op == "step":
+            got, full = _both(lambda: cpp.append_step(a, b), lambda: model.append_step(a, b))
+            if not full:
+                (slots, cows), (want_slots, want_cows) = got
+                assert list(slots) == want_slots
+                assert [tuple(int(x) for x in c) for c in cows] == want_cows
+                steps += 1
         elif op == "fork":
-            if a not in live:
-                continue
             model.fork(a, b)
             cpp.fork(a, b)
             live.append(b)
+        elif op == "swap_out":
+            assert list(cpp.swap_out(a)) == model.swap_out(a)
+            live.remove(a)
+            out.append(a)
+            swaps += 1
+        elif op == "swap_in":
+            got, full = _both(lambda: cpp.swap_in(a), lambda: model.swap_in(a))
+            if not full:
+                ids, want = got
+                assert list(ids) == want
+                out.remove(a)
+                live.append(a)
         else:
-            if a not in live:
-                continue
             model.free_sequence(a)
             cpp.free_sequence(a)
-            live.remove(a)
+            (live if a in live else out).remove(a)
+        exhausted += full if op in ("add", "append", "step", "swap_in") else 0
         _same_state(cpp, model, live, 4096)
     assert exhausted > 0 or nb == 200      # the small pools do run out
+    assert swaps > 0 and steps > 0
+
+
+def test_decode_step_is_all_or_nothing():
+    """Two forks of a sequence with a shared partly filled last block: in one
+    step the first writer copies it, the second then holds it alone."""
+    for mgr in (obm.BlockManagerModel(6, 4), _lib.BlockManager(6, 4)):
+        mgr.add_sequence(1, [1, 2, 3, 4, 5, 6])        # blocks 0, 1 (half full)
+        mgr.fork(1, 2)
+        mgr.fork(1, 3)                                  # block 1 held three times
+        slots, cows = mgr.append_step([2, 3, 1], [7, 7, 7])
+        assert [tuple(int(x) for x in c) for c in cows] == [(1, 2), (1, 3)]
+        assert list(slots) == [2 * 4 + 2, 3 * 4 + 2, 1 * 4 + 2]
+        # 2 free blocks left; a step that needs 3 new blocks changes nothing
+        for sid in (1, 2, 3):
+            mgr.append(sid, [8])                        # all last blocks now full
+        free = mgr.num_free()
+        assert free == 2
+        with pytest.raises((MemoryError, _lib.PagedKVError)):
+            mgr.append_step([1, 2, 3], [9, 9, 9])
+        assert mgr.num_free() == free
+
+
+def test_swap_out_and_back_in():
+    for mgr in (obm.BlockManagerModel(8, 4), _lib.BlockManager(8, 4)):
+        mgr.add_sequence(1, list(range(10)))            # blocks 0, 1, 2
+        mgr.add_sequence(2, list(range(100, 105)))      # blocks 3, 4
+        assert list(mgr.swap_out(1)) == [0, 1, 2]
+        assert mgr.num_free() == 6
+        with pytest.raises((KeyError, _lib.PagedKVError)):
+            mgr.append(1, [1])                          # swapped out: only swap_in or free
+        # released last block first: 2 to the plain free list, full blocks
+        # 1 then 0 stay cached but free
+        mgr.append(2, [1, 2, 3, 4])                     # block 4 fills; takes block 2
+        assert list(mgr.swap_in(1)) == [5, 6, 7]        # plain free blocks before cached ones
+        assert mgr.num_free() == 2                      # cached 0, 1
+        assert list(mgr.swap_out(2)) == [3, 4, 2]
+        assert mgr.stats()["blocks_in_use"] == 3
 
 
 def test_cpp_manager_rejects_bad_calls():

@@ -1,8 +1,9 @@
 """The host block manager driving the device path (needs an MI355X).
 
 A small serving loop: prompts that share a system prompt (prefix-cache
-reuse), forks whose next token triggers copy-on-write, frees, and new
-sequences that land in released and evicted blocks.  Every step the manager's
+reuse), forks whose next token triggers copy-on-write, frees, new sequences
+that land in released and evicted blocks, and a sequence swapped out to host
+memory while others reuse its blocks, then swapped back into other blocks.  Every step the manager's
 slots, copy-on-write pairs and block tables feed paged_copy_blocks,
 paged_kv_append and paged_attention_decode; the outputs are compared with
 attention over each sequence's logical K/V kept on the host, which involves
@@ -62,7 +63,6 @@ def test_block_manager_drives_decode():
     dev = torch.device("cuda", 0)
     kc = torch.zeros((NB, H_KV, BS, D), dtype=torch.bfloat16, device=dev)
     vc = torch.zeros_like(kc)
-    pool = _lib.pool_of(kc)
     tokens = {}      # seq id -> token ids
     logical = {}     # seq id -> [K list, V list]
     cow_pairs = []
@@ -101,12 +101,18 @@ def test_block_manager_drives_decode():
         tokens[child] = list(tokens[parent])
         logical[child] = [list(logical[parent][0]), list(logical[parent][1])]
 
+    swapped = {}     # seq id -> host image
+
     def decode_all(step):
-        live = sorted(tokens)
-        for sid in live:
-            tok = int(rng.integers(0, 1000))
-            slots, cow = bm.append(sid, [tok])
-            write(sid, [tok], slots, cow)
+        live = sorted(set(tokens) - set(swapped))
+        toks = [int(t) for t in rng.integers(0, 1000, size=len(live))]
+        slots, cows = bm.append_step(live, toks)
+        for c in cows:                  # every copy lands before any of the step's writes
+            cow_pairs.append(tuple(int(x) for x in c))
+        if len(cows):
+            _lib.paged_copy_blocks(kc, vc, to_dev(np.ascontiguousarray(cows), DT))
+        for sid, tok, slot in zip(live, toks, slots):
+            write(sid, [tok], [slot], None)
         bt, lens = bm.build_batch(live, 64)
         q = rng.standard_normal((len(live), H_Q, D)).astype(np.float32)
         q_st = torch.from_numpy(q).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
@@ -131,6 +137,15 @@ def test_block_manager_drives_decode():
             del tokens[0], logical[0]
         if step == 12:
             add(20, system + [7, 7, 7])
+        if step == 14:
+            ids = bm.swap_out(3)
+            swapped[3] = _lib.paged_swap_out(kc, vc, to_dev(ids, DT))
+            torch.cuda.synchronize()
+        if step == 15:                  # takes blocks sequence 3 gave up
+            add(21, list(rng.integers(0, 1000, size=60)))
+        if step == 19:
+            ids = bm.swap_in(3)
+            _lib.paged_swap_in(swapped.pop(3), kc, vc, to_dev(ids, DT))
         decode_all(step)
     assert len(cow_pairs) >= 2          # each fork's first write copied the shared block
     st = bm.stats()

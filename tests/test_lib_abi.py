@@ -109,3 +109,18 @@ def test_append_and_copy_reject_bad_arguments(lib):
     assert lib.paged_copy_blocks(FAKE, FAKE, p, FAKE, -2, None) == 1
     assert lib.paged_copy_blocks(None, None, p, None, 0, None) == 0
     assert lib.pkv_stream_copy(FAKE, FAKE, 24, None) == 1
+
+
+def test_swap_rejects_bad_arguments(lib):
+    p = _pool()                         # bf16, H_kv 2, bs 16, D 64: 4096-byte tiles
+    entry = 2 * 2 * 16 * 64 * 2
+    out, inn = lib.paged_swap_out, lib.paged_swap_in
+    assert out(FAKE, FAKE, p, FAKE, -1, FAKE, FAKE, entry, None) == 1
+    assert out(None, None, p, None, 0, None, None, 0, None) == 0            # nothing to move
+    assert out(FAKE, FAKE, p, FAKE, 3, None, FAKE, entry, None) == 1        # no host image
+    assert out(FAKE, FAKE, p, FAKE, 3, FAKE, FAKE, entry - 16, None) == 3   # staging < one block
+    assert out(FAKE, FAKE, _pool(bs=8), FAKE, 3, FAKE, FAKE, entry, None) == 2
+    assert inn(FAKE, 3, FAKE, FAKE, p, FAKE, ctypes.c_void_p(0x1008), entry, None) == 1  # alignment
+    assert inn(FAKE, 3, FAKE, FAKE, p, None, FAKE, entry, None) == 1        # no ids
+    assert inn(FAKE, -4, FAKE, FAKE, p, FAKE, FAKE, entry, None) == 1
+    assert inn(None, 0, None, None, p, None, None, 0, None) == 0

@@ -511,3 +511,68 @@ def test_pins_reject_planted_mistakes(kind):
     ok = _mutant_decode("none")(c["q"], c["kpool"], c["vpool"], c["bt"], c["ctx"], scale, "f32")
     assert np.max(np.abs(ok - ref)) <= 1e-12
     assert not (np.max(np.abs(bad - ref)) <= 1e-12)
+
+
+# ---------------------------------------------------------------------------
+# swap to host memory and back
+# ---------------------------------------------------------------------------
+
+def _coordinate_pools(NB, H, bs, D):
+    """Pools whose every element encodes its own (K or V, block, head, token,
+    dim), so an image element tells where it was read from."""
+    kv, b, h, t, d = np.meshgrid(np.arange(2), np.arange(NB), np.arange(H), np.arange(bs),
+                                 np.arange(D), indexing="ij")
+    code = ((((kv * 100 + b) * 10 + h) * 100 + t) * 100 + d).astype(np.uint32)
+    return code[0], code[1]
+
+
+def test_swap_out_image_entries_name_their_source():
+    NB, H, bs, D = 7, 3, 4, 5
+    kpool, vpool = _coordinate_pools(NB, H, bs, D)
+    ids = [5, 0, 5, 3]
+    img = oracle.swap_out(kpool, vpool, ids)
+    assert img.shape == (4, 2, H, bs, D)
+    for i, b in enumerate(ids):
+        for kv in range(2):
+            for h in range(H):
+                for t in range(bs):
+                    for d in range(D):
+                        want = (((kv * 100 + b) * 10 + h) * 100 + t) * 100 + d
+                        assert img[i, kv, h, t, d] == want
+    # ids outside the pool give zero entries
+    img = oracle.swap_out(kpool, vpool, [NB, -1, 2])
+    assert not img[0].any() and not img[1].any()
+    assert img[2, 1, 2, 3, 4] == (((100 + 2) * 10 + 2) * 100 + 3) * 100 + 4
+
+
+def test_swap_round_trip_and_moved_blocks_keep_attention():
+    """A sequence swapped out and brought back into other blocks, with its
+    table rewritten, attends exactly as before; blocks not named are left
+    alone."""
+    rng = np.random.default_rng(17)
+    H_q, H_kv, D, bs, NB = 4, 2, 8, 4, 12
+    kpool = rng.standard_normal((NB, H_kv, bs, D)).astype(np.float32)
+    vpool = rng.standard_normal((NB, H_kv, bs, D)).astype(np.float32)
+    q = rng.standard_normal((1, H_q, D)).astype(np.float32)
+    table = np.array([[3, 9, 1]], dtype=np.int32)
+    ctx = np.array([10], dtype=np.int32)
+    before = oracle.decode_attention(q, kpool, vpool, table, ctx, 0.3, "f32")
+    img = oracle.swap_out(kpool, vpool, table[0])
+    # the pool is reused meanwhile: scribble over the old blocks
+    wiped_k, wiped_v = kpool.copy(), vpool.copy()
+    wiped_k[[3, 9, 1]] = np.nan
+    wiped_v[[3, 9, 1]] = np.nan
+    new_ids = [0, 11, 6]
+    k2, v2 = oracle.swap_in(wiped_k, wiped_v, img, new_ids)
+    after = oracle.decode_attention(q, k2, v2, np.array([new_ids], dtype=np.int32), ctx, 0.3, "f32")
+    assert np.array_equal(before, after)
+    for b in range(NB):
+        if b not in new_ids:
+            assert np.array_equal(k2[b], wiped_k[b], equal_nan=True)
+    # swap_in of the image at the original ids is the identity on those blocks
+    k3, v3 = oracle.swap_in(wiped_k, wiped_v, img, table[0])
+    assert np.array_equal(k3[table[0]], kpool[table[0]]) and np.array_equal(v3[table[0]], vpool[table[0]])
+    with pytest.raises(ValueError):
+        oracle.swap_in(kpool, vpool, img, [2, 2, 4])
+    k4, _ = oracle.swap_in(kpool, vpool, img, [NB, -1, 4])       # outside the pool: skipped
+    assert np.array_equal(k4[4], kpool[1]) and np.array_equal(np.delete(k4, 4, 0), np.delete(kpool, 4, 0))
