@@ -715,14 +715,6 @@ struct SlotMeta {
   int p;
 };
 
-// 64 block ids of sequence s starting at its logical block blk0 (lane i holds
-// block blk0 + i, -1 past the sequence's last block).
-__device__ __forceinline__ int load_id_batch(const AttnParams& prm, int s, int blk0, int nblk,
-                                             int lane) {
-  const int j = blk0 + lane;
-  return j < nblk ? prm.block_tables[(size_t)s * prm.max_blocks_per_seq + j] : -1;
-}
-
 // Query operand of column group cg (B of the QK MFMA): lane (r, col) holds
 // column c = 16*cg + col, i.e. new token c / G of the sequence and query head
 // h*G + c % G, 16-byte chunks r + 4*kk of that row; zero for columns past
@@ -843,21 +835,16 @@ void attn_stream_kernel(AttnParams prm) {
   int pi = a;
   SeqSpan si;
   SeqCols ci;
-  int nblk_i = 0, blk0_i = 0, ids_i = -1;
-  // Block ids arrive in 64-entry batches.  The wait for a batch is taken
-  // where it is loaded (a group entry, or every 64 blocks): loads issued on
-  // some paths only would otherwise make the wait at every lookup drain the
-  // tiles in flight.
-  auto load_ids_now = [&]() {
-    ids_i = load_id_batch(prm, si.s, blk0_i, nblk_i, lane);
-    asm volatile("" : "+v"(ids_i));
-  };
+  // Block ids are read one at a time with scalar loads through the constant
+  // address space: the index is wave-uniform, the row stays in the scalar
+  // cache, and the scalar counter keeps the vector loads of the tiles in
+  // flight (a vector load of the ids, used right away, drained them).
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const_i32* row_i = nullptr;
   auto enter_issue_seq = [&]() {
     si = locate<MULTI>(pi, per, sS, sCtx, B);
     ci = seq_cols<MULTI>(sCtx, sQS, sQL, si.s, G);
-    nblk_i = (ci.n + BS - 1) / BS;
-    blk0_i = (pi - si.A) * kSub / BS;
-    load_ids_now();
+    row_i = (const_i32*)prm.block_tables + (size_t)si.s * prm.max_blocks_per_seq;
   };
   auto issue = [&](Tile<N>& t, SlotMeta& m) {
     if (pi < b) {
@@ -865,12 +852,9 @@ void attn_stream_kernel(AttnParams prm) {
       // all wave-uniform; readfirstlane keeps them (and the resources built
       // from them) in scalar registers
       const int tsub = uniform(pi - si.A);
+      // blk < ceil(n / BS) <= max_blocks_per_seq: inside the sequence's row
       const int blk = tsub * kSub / BS;
-      if (blk - blk0_i >= 64) {
-        blk0_i = blk;
-        load_ids_now();
-      }
-      int phys = __builtin_amdgcn_readlane(ids_i, blk - blk0_i);
+      int phys = row_i[blk];
       const bool ok = (unsigned)phys < (unsigned)prm.num_blocks;
       phys = ok ? phys : 0;
       int rows;
