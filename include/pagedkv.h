@@ -153,9 +153,9 @@ PKV_API pkv_status paged_attention_decode(void* out, const void* q,
 
 /*
  * Bytes of workspace paged_attention_multi needs for this shape on the
- * current device, or 0 for invalid input or a call it refuses (more than 2048
- * sequences, or more than 2^28 positions: kv heads x 16-column groups x
- * 16-token sub-tiles).
+ * current device, or 0 for invalid input, for a call it refuses, or for a
+ * call that takes the prefill path (max_query_len * G >= 64), which needs
+ * none.
  */
 PKV_API size_t paged_attention_multi_workspace_bytes(pkv_pool pool, int32_t num_seqs,
                                                      int32_t num_q_heads, int32_t max_query_len,
@@ -175,22 +175,31 @@ PKV_API size_t paged_attention_multi_workspace_bytes(pkv_pool pool, int32_t num_
  *     out[row, h, :] = softmax_t(scale * q[row, h, :] . K_s[h/G, t, :]) @ V_s[h/G, t, :],
  *                      t <= n - L + i
  *
- * With L = 1 for every sequence this is paged_attention_decode.  The kernel's
- * MFMA columns are (new token, query head) pairs in groups of 16; each group
- * streams the sequence's context once, so L * G <= 16 (e.g. 4 draft tokens
- * at G = 4) reads every K/V byte once, and longer chunks re-read it once per
- * further group.  Precision, determinism and metadata trust as for
- * paged_attention_decode; rows of a sequence are clamped to
- * [0, num_query_tokens] and to at most min(n, max_query_len), so malformed
- * query_start values never move a read or write outside its buffer.
+ * With L = 1 for every sequence this is paged_attention_decode.  The MFMA
+ * columns are (new token, query head) pairs in groups of 16.  Two paths:
+ *  - max_query_len * G < 64 (speculative verification, mixed small chunks):
+ *    the decode kernel's stream of sub-tiles, one pass over the context per
+ *    column group (L * G <= 16, e.g. 4 draft tokens at G = 4, reads every
+ *    K/V byte once), partial states merged afterwards; num_seqs <= 2048,
+ *    at most 2^28 positions (kv heads x column groups x 16-token sub-tiles);
+ *  - max_query_len * G >= 64 (prompt chunks): one workgroup per (sequence,
+ *    kv head, four column groups) streams the context once through LDS for
+ *    64 columns and writes its rows directly; no workspace; num_seqs <=
+ *    65535; up to 256 sequences are dispatched longest context first.
+ * Both give the same result up to fp32 rounding order.  Precision,
+ * determinism and metadata trust as for paged_attention_decode; rows of a
+ * sequence are clamped to [0, num_query_tokens] and to at most
+ * min(n, max_query_len), so malformed query_start values never move a read
+ * or write outside its buffer.
  *
  *   out, q        [num_query_tokens, num_q_heads, head_dim]  pool dtype, rows
  *                 packed sequence by sequence (no padding)
  *   query_start   [num_seqs + 1] int32 device prefix of query rows,
  *                 query_start[0] = 0, non-decreasing, last = num_query_tokens
  *   max_query_len host-known upper bound of L over the batch
- *   other arguments as for paged_attention_decode; num_seqs <= 2048
- *   workspace     >= paged_attention_multi_workspace_bytes(...) bytes
+ *   other arguments as for paged_attention_decode
+ *   workspace     >= paged_attention_multi_workspace_bytes(...) bytes (may be
+ *                 NULL when that is 0)
  */
 PKV_API pkv_status paged_attention_multi(void* out, const void* q,
                                          const void* k_cache, const void* v_cache,

@@ -224,15 +224,14 @@ __device__ __forceinline__ void restage_k(uint4 (&a)[N], const Tile<N>& t, char*
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// QK, mask, online softmax and PV of one 16-token sub-tile; `valid` tokens
-// (from the sub-tile's first) are real, the rest are masked.  `lds` is this
-// wave's private staging slot (at least one sub-tile of K).
+// QK, mask, online softmax and PV of one 16-token sub-tile whose K is in the
+// MFMA A operand order (ka) and V in its load order (vv); `valid` tokens
+// (from the sub-tile's first) are real for this lane's column, the rest are
+// masked.
 template <int DT, int N, int kMM>
-__device__ __forceinline__ void attend_subtile(Tile<N>& t, const uint4 (&qb)[N], int valid,
-                                               float scale_log2, int r, WaveState<kMM>& st,
-                                               char* lds) {
-  uint4 ka[N];
-  restage_k<N>(ka, t, lds, threadIdx.x & 63);
+__device__ __forceinline__ void attend_core(const uint4 (&ka)[N], const uint32_t (&vv)[4][N],
+                                            const uint4 (&qb)[N], int valid, float scale_log2,
+                                            int r, WaveState<kMM>& st) {
   // ---- QK on MFMA ----------------------------------------------------------
   floatx4 S = {0.f, 0.f, 0.f, 0.f};
   if constexpr (DT == DT_F32) {
@@ -282,7 +281,7 @@ __device__ __forceinline__ void attend_subtile(Tile<N>& t, const uint4 (&qb)[N],
     for (int mm = 0; mm < kMM; ++mm) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        st.acc[mm] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.v[e][mm]), pe[e],
+        st.acc[mm] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[e][mm]), pe[e],
                                                           st.acc[mm], 0, 0, 0);
     }
   } else {
@@ -315,8 +314,8 @@ __device__ __forceinline__ void attend_subtile(Tile<N>& t, const uint4 (&qb)[N],
       const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
       const int wd = mm >> 1;
       uint2 a;
-      a.x = __builtin_amdgcn_perm(t.v[1][wd], t.v[0][wd], sel);
-      a.y = __builtin_amdgcn_perm(t.v[3][wd], t.v[2][wd], sel);
+      a.x = __builtin_amdgcn_perm(vv[1][wd], vv[0][wd], sel);
+      a.y = __builtin_amdgcn_perm(vv[3][wd], vv[2][wd], sel);
       if constexpr (DT == DT_BF16) {
         const shortx4 A = __builtin_bit_cast(shortx4, a);
         st.acc[mm] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(shortx4, phi),
@@ -332,6 +331,17 @@ __device__ __forceinline__ void attend_subtile(Tile<N>& t, const uint4 (&qb)[N],
       }
     }
   }
+}
+
+// attend_core for a sub-tile as loaded: K is re-dealt through `lds`, this
+// wave's private staging slot (at least one sub-tile of K).
+template <int DT, int N, int kMM>
+__device__ __forceinline__ void attend_subtile(Tile<N>& t, const uint4 (&qb)[N], int valid,
+                                               float scale_log2, int r, WaveState<kMM>& st,
+                                               char* lds) {
+  uint4 ka[N];
+  restage_k<N>(ka, t, lds, threadIdx.x & 63);
+  attend_core<DT, N, kMM>(ka, t.v, qb, valid, scale_log2, r, st);
 }
 
 template <int DT, int D, int BS>
@@ -1047,11 +1057,234 @@ __global__ __launch_bounds__(64) void attn_stream_merge_kernel(AttnParams prm) {
 // Launch
 // ===========================================================================
 
+// ===========================================================================
+// Prefill path: many new tokens per sequence
+// ===========================================================================
+//
+// With L new tokens a sequence has ceil(L * G / 16) column groups; the stream
+// kernel streams its context once per group, so a 256-token chunk at G = 4
+// reads every K/V byte 64 times.  Here a workgroup takes four consecutive
+// column groups of one (sequence, kv head), one per wave, and streams the
+// context once for all four: per stage each wave loads one 16-token sub-tile
+// (the block table row read with scalar loads), parks it in LDS (K in the
+// A-operand staging order, V in its load order), and after a barrier every
+// wave runs QK, online softmax and PV over the stage's four sub-tiles for its
+// own 16 columns.  The next three stages' loads are in flight meanwhile.  The
+// workgroup covers the whole context, so it writes the output rows directly.
+// Grid: column block x kv head x sequence rank; blocks past a sequence's
+// columns exit at once.
+
+template <int DT, int D, int BS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_prefill_kernel(AttnParams prm) {
+  using Geo = Geometry<DT, D, BS>;
+  constexpr int N = Geo::N;
+  constexpr int kMM = Geo::kMM;
+  constexpr int kRow = Geo::kRow;
+  constexpr int kSubBytes = kSub * kRow;
+  constexpr int kSwz = (4 * N - 1) < 15 ? (4 * N - 1) : 15;
+  __shared__ __attribute__((aligned(16))) char sK[2][kWaves][kSubBytes];
+  __shared__ __attribute__((aligned(16))) char sV[2][kWaves][kSubBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int r = lane >> 4;
+  const int h = (int)blockIdx.y;
+  const int cb = (int)blockIdx.x;
+  const int G = prm.group;
+  const int Hq = prm.num_q_heads;
+
+  // Longest context first: with up to kPrefillRankSeqs sequences, grid row z
+  // takes the sequence whose context is the z-th longest (ties by index), so
+  // that the longest workgroups are dispatched first instead of trailing.
+  int s = (int)blockIdx.z;
+  if (prm.num_seqs <= kPrefillRankSeqs) {
+    __shared__ int sN[kPrefillRankSeqs];
+    __shared__ int sPick;
+    const int B = prm.num_seqs;
+    if (tid < B) {
+      int c = prm.context_lens[tid];
+      sN[tid] = c < 0 ? 0 : (c > prm.max_context_len ? prm.max_context_len : c);
+    }
+    __syncthreads();
+    if (tid < B) {
+      const int mine = sN[tid];
+      int rank = 0;
+      for (int j = 0; j < B; ++j) rank += (sN[j] > mine) || (sN[j] == mine && j < tid);
+      if (rank == (int)blockIdx.z) sPick = tid;
+    }
+    __syncthreads();
+    s = uniform(sPick);
+  }
+
+  // the sequence's rows, clamped exactly as on the stream path
+  int n = prm.context_lens[s];
+  n = uniform(n < 0 ? 0 : (n > prm.max_context_len ? prm.max_context_len : n));
+  const int T = prm.num_query_tokens;
+  int q0 = prm.query_start[s], qe = prm.query_start[s + 1];
+  q0 = q0 < 0 ? 0 : (q0 > T ? T : q0);
+  qe = qe < q0 ? q0 : (qe > T ? T : qe);
+  int L = qe - q0;
+  L = L < n ? L : n;
+  L = L < prm.max_query_len ? L : prm.max_query_len;
+  q0 = uniform(q0);
+  L = uniform(L);
+  const int ngrp = (L * G + kSub - 1) / kSub;
+  if (cb * kWaves >= ngrp) return;  // the whole workgroup: no barrier follows
+
+  SeqCols sc;
+  sc.n = n;
+  sc.L = L;
+  sc.q0 = q0;
+  sc.ngrp = ngrp;
+  const int cg = cb * kWaves + w;
+  uint4 qb[N];
+  load_query_cols<N, true>(qb, prm.q, sc, h, cg, G, Hq, lane);
+  const int col = cg * kSub + (lane & 15);
+  const int vis = col < L * G ? n - L + col / G + 1 : 0;  // tokens this lane's column sees
+  // tokens the last column of this wave's group / of the block's last group sees
+  auto group_limit = [&](int g) {
+    int i_last = (g * kSub + kSub - 1) / G;
+    i_last = i_last < L - 1 ? i_last : L - 1;
+    return n - L + i_last + 1;
+  };
+  const int nsub_w = cg < ngrp ? (group_limit(cg) + kSub - 1) / kSub : 0;
+  const int cg_last = (cb + 1) * kWaves < ngrp ? (cb + 1) * kWaves - 1 : ngrp - 1;
+  const int rows_b = group_limit(cg_last);
+  const int nsub_b = (rows_b + kSub - 1) / kSub;
+  const int nstage = (nsub_b + kWaves - 1) / kWaves;
+
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const_i32* row_ids = (const_i32*)prm.block_tables + (size_t)s * prm.max_blocks_per_seq;
+  const int koff = 16 * lane;
+  const int voff = (4 * r) * kRow + (lane & 15) * (4 * N);
+
+  // Sub-tile `sub` of the context into t; past the block's last visible row
+  // (or for an id outside the pool) the rows read as zeros, touching nothing.
+  auto load_sub = [&](Tile<N>& t, int sub) {
+    const char* kb = static_cast<const char*>(prm.k_cache);
+    const char* vb = static_cast<const char*>(prm.v_cache);
+    int nrec = 0;
+    if (sub < nsub_b) {
+      const int blk = sub * kSub / BS;  // < ceil(rows_b / BS) <= max_blocks_per_seq
+      int phys = row_ids[blk];
+      const bool ok = (unsigned)phys < (unsigned)prm.num_blocks;
+      phys = ok ? phys : 0;
+      int rows = rows_b - sub * kSub;
+      rows = rows > kSub ? kSub : rows;
+      const size_t off = ((size_t)phys * prm.num_kv_heads + h) * Geo::kTileBytes +
+                         (sub * kSub % BS) * kRow;
+      nrec = uniform(ok ? rows * kRow : 0);
+      kb += off;
+      vb += off;
+    }
+    load_tile<N>(t, make_rsrc(kb, nrec), make_rsrc(vb, nrec), koff, voff);
+  };
+  // This wave's loaded sub-tile into slot w of stage buffer b: K chunk c of
+  // token row t at chunk position c ^ (t & mask) (as restage_k stores it),
+  // V as the lanes hold it.
+  auto park = [&](const Tile<N>& t, int b) {
+#pragma unroll
+    for (int kk = 0; kk < N; ++kk) {
+      const int o = 1024 * kk + 16 * lane;
+      const int tr = o / kRow, c = (o % kRow) / 16;
+      *reinterpret_cast<uint4*>(&sK[b][w][tr * kRow + ((c ^ (tr & kSwz)) * 16)]) = t.k[kk];
+    }
+#pragma unroll
+    for (int qd = 0; qd < N; ++qd)
+      *reinterpret_cast<uint4*>(&sV[b][w][(qd * 64 + lane) * 16]) =
+          make_uint4(t.v[0][qd], t.v[1][qd], t.v[2][qd], t.v[3][qd]);
+  };
+
+  WaveState<kMM> st;
+  st.reset();
+  const float scale_log2 = prm.scale_log2;
+  // QK, softmax and PV over the four sub-tiles of stage sg (LDS buffer b).
+  auto compute_stage = [&](int sg, int b) {
+#pragma unroll
+    for (int j = 0; j < kWaves; ++j) {
+      const int sub = sg * kWaves + j;
+      if (sub < nsub_w) {
+        uint4 ka[N];
+        uint32_t vv[4][N];
+        const int tr = lane & 15;
+#pragma unroll
+        for (int kk = 0; kk < N; ++kk) {
+          const int c = (lane >> 4) + 4 * kk;
+          ka[kk] = *reinterpret_cast<const uint4*>(&sK[b][j][tr * kRow + ((c ^ (tr & kSwz)) * 16)]);
+        }
+#pragma unroll
+        for (int qd = 0; qd < N; ++qd) {
+          const uint4 x = *reinterpret_cast<const uint4*>(&sV[b][j][(qd * 64 + lane) * 16]);
+          vv[0][qd] = x.x;
+          vv[1][qd] = x.y;
+          vv[2][qd] = x.z;
+          vv[3][qd] = x.w;
+        }
+        int valid = vis - sub * kSub;
+        valid = valid > kSub ? kSub : valid;
+        attend_core<DT, N, kMM>(ka, vv, qb, valid, scale_log2, r, st);
+      }
+    }
+  };
+  // A ring of three register tiles keeps this wave's sub-tiles of the next
+  // three stages in flight: at stage sg the load of stage sg + 3 is issued,
+  // stage sg is computed from LDS, and stage sg + 1 is parked in the other
+  // buffer (whose last readers finished before the previous barrier).
+  Tile<N> t0, t1, t2;
+  load_sub(t0, w);
+  load_sub(t1, kWaves + w);
+  load_sub(t2, 2 * kWaves + w);
+  park(t0, 0);
+  __syncthreads();
+  // Rounds of three stages with no exit in between: every path issues the
+  // same loads, so each park waits for its own tile only.  Stages past the
+  // end load nothing and compute nothing.
+  for (int sg = 0; sg < nstage; sg += 3) {
+    load_sub(t0, (sg + 3) * kWaves + w);
+    compute_stage(sg, sg & 1);
+    park(t1, (sg + 1) & 1);
+    __syncthreads();
+    load_sub(t1, (sg + 4) * kWaves + w);
+    if (sg + 1 < nstage) compute_stage(sg + 1, (sg + 1) & 1);
+    park(t2, (sg + 2) & 1);
+    __syncthreads();
+    load_sub(t2, (sg + 5) * kWaves + w);
+    if (sg + 2 < nstage) compute_stage(sg + 2, (sg + 2) & 1);
+    park(t0, (sg + 3) & 1);
+    __syncthreads();
+  }
+
+  if (cg < ngrp) {
+    float l = st.l + __shfl_xor(st.l, 16);
+    l += __shfl_xor(l, 32);
+    float o[D / 4];
+    lane_run<D, kMM>(o, st);
+    if (col < L * G) {
+      const size_t orow = (size_t)(q0 + col / G) * Hq + (size_t)h * G + col % G;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i) o[i] *= inv;
+      store_run<DT, D>(static_cast<char*>(prm.out) + (orow * D + r * (D / 4)) * Geo::EB, o);
+    }
+  }
+}
+
 template <int DT, int D, int BS>
 hipError_t launch_typed(const AttnParams& prm, hipStream_t stream) {
   const dim3 block(kThreads);
   const long long nout = (long long)prm.num_seqs * prm.num_q_heads;
   if (nout > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (prm.prefill_blocks > 0) {
+    if (!prm.query_start || prm.num_seqs > 65535 || prm.num_kv_heads > 65535)
+      return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((attn_prefill_kernel<DT, D, BS>),
+                       dim3((unsigned)prm.prefill_blocks, (unsigned)prm.num_kv_heads,
+                            (unsigned)prm.num_seqs),
+                       block, 0, stream, prm);
+    return hipGetLastError();
+  }
   if (prm.stream_wgs > 0) {
     const long long nmerge =
         (long long)prm.num_seqs * prm.num_kv_heads * prm.max_groups * prm.slot_cols;

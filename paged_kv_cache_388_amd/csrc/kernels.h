@@ -23,6 +23,12 @@ constexpr int kStreamWaves = 4;           // waves per workgroup
 constexpr int kMaxStreamSeqs = 4096;      // batch limit (per-sequence tables live in LDS)
 constexpr int kMinChunk = 4;              // sub-tiles per wave at least
 constexpr int kMaxMultiSeqs = 2048;       // batch limit with several new tokens per sequence
+// Multi-token calls with at least this many columns (max_query_len * G) per
+// sequence take the prefill path.
+constexpr int kPrefillMinCols = 64;
+// Up to this many sequences the prefill path dispatches them longest context
+// first (each workgroup ranks the context lengths itself).
+constexpr int kPrefillRankSeqs = 256;
 // Positions (H_kv x sub-tiles of the batch) the stream path indexes in 32 bits;
 // the host sends calls whose bound B * ceil(max_ctx / 16) * H_kv exceeds it to
 // the grid path.
@@ -64,6 +70,9 @@ struct AttnParams {
   int32_t max_query_len;        // host-known bound of the new tokens per sequence
   int32_t max_groups;           // ceil(max_query_len * G / 16)
   int32_t slot_cols;            // columns per partial slot: min(16, max_query_len * G)
+  // > 0: prefill path, this many workgroups per (sequence, kv head), each
+  // taking four 16-column groups (ceil(max_groups / 4)); no workspace.
+  int32_t prefill_blocks;
 };
 
 // Workspace layout of one decode call, shared by the size query and the call.

@@ -90,6 +90,11 @@ int32_t stream_wgs_for(int32_t num_seqs, int32_t num_kv_heads, int32_t max_conte
 int32_t max_groups_for(int32_t max_query_len, int32_t group) {
   return (int32_t)(((long long)max_query_len * group + pkv::kSubTokens - 1) / pkv::kSubTokens);
 }
+// Multi-token calls whose longest sequence has at least kPrefillMinCols
+// (new token, query head) columns take the prefill path.
+bool prefill_route(int32_t max_query_len, int32_t group) {
+  return (long long)max_query_len * group >= pkv::kPrefillMinCols;
+}
 int32_t slot_cols_for(int32_t max_query_len, int32_t group) {
   const long long c = (long long)max_query_len * group;
   return (int32_t)(c < pkv::kSubTokens ? c : pkv::kSubTokens);
@@ -153,6 +158,7 @@ size_t attention_workspace(const pkv_pool& pool, int32_t num_seqs, int32_t num_q
     return 0;
   const int32_t group = num_q_heads / pool.num_kv_heads;
   const int32_t groups = max_groups_for(max_query_len, group);
+  if (multi && prefill_route(max_query_len, group)) return 0;
   const int32_t wgs = stream_wgs_for(num_seqs, pool.num_kv_heads, max_context_len, groups, multi);
   if (multi && wgs == 0) return 0;
   return pkv::attn_workspace_layout(num_seqs, slot_cols_for(max_query_len, group), num_q_heads,
@@ -195,16 +201,21 @@ pkv_status attention_call(const char* what, void* out, const void* q, const void
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_EINVAL, "out, q and the pools must be 16-byte aligned");
   const int32_t groups = max_groups_for(max_query_len, group);
+  const bool prefill = multi && prefill_route(max_query_len, group);
+  if (prefill && num_seqs > 65535)
+    return fail(PKV_EUNSUPPORTED, "the prefill path takes at most 65535 sequences");
   const int32_t stream_wgs =
-      stream_wgs_for(num_seqs, pool.num_kv_heads, max_context_len, groups, multi);
-  if (multi && stream_wgs == 0)
+      prefill ? 0 : stream_wgs_for(num_seqs, pool.num_kv_heads, max_context_len, groups, multi);
+  if (multi && !prefill && stream_wgs == 0)
     return fail(PKV_EUNSUPPORTED,
                 "multi-token attention takes at most %d sequences and 2^28 positions "
                 "(kv heads x 16-column groups x 16-token sub-tiles)",
                 pkv::kMaxMultiSeqs);
   const int32_t cols = slot_cols_for(max_query_len, group);
-  const pkv::AttnWorkspace lay = pkv::attn_workspace_layout(
-      num_seqs, cols, num_q_heads, pool.head_dim, max_context_len, stream_wgs);
+  const pkv::AttnWorkspace lay =
+      prefill ? pkv::AttnWorkspace{0, 0, 0, 0}
+              : pkv::attn_workspace_layout(num_seqs, cols, num_q_heads, pool.head_dim,
+                                           max_context_len, stream_wgs);
   if (lay.bytes > 0 && (!workspace || workspace_bytes < lay.bytes))
     return fail(PKV_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, lay.bytes);
   if (lay.bytes > 0 && !aligned16(workspace)) return fail(PKV_EINVAL, "workspace must be 16-byte aligned");
@@ -235,6 +246,7 @@ pkv_status attention_call(const char* what, void* out, const void* q, const void
   prm.max_query_len = multi ? max_query_len : 1;
   prm.max_groups = groups;
   prm.slot_cols = cols;
+  prm.prefill_blocks = prefill ? (groups + pkv::kStreamWaves - 1) / pkv::kStreamWaves : 0;
   hipError_t err = pkv::launch_paged_attention(prm, pool.dtype, pool.head_dim, pool.block_size, stream);
   return err == hipSuccess ? PKV_OK : hip_fail(err, what);
 }

@@ -101,3 +101,55 @@ def test_full_size_multi_workloads(name):
     w = wl.named(name)
     err = _run(w, name)
     print(f"[gpu] {name}: max |gpu - oracle| = {err:.3e}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# the prefill path (max_query_len * G >= 64): one workgroup per (sequence,
+# kv head, 64 columns), longest context first up to 256 sequences
+# ---------------------------------------------------------------------------
+
+def test_prefill_path_ranked_ties_and_mixed_lengths():
+    """Equal contexts (rank ties), sequences with 0, 1 and many new tokens,
+    a chunk longer than one 64-column block, an empty context."""
+    rng = np.random.default_rng(48)
+    ctx = [700, 700, 65, 1300, 0, 700, 31]
+    ql = [40, 1, 17, 64, 0, 0, 31]
+    w = wl.build("pf_mixed", 48, rng, ctx, 8, 2, 128, 16, "bf16", poison=True, query_lens=ql)
+    assert w.max_query_len * 4 >= 64
+    assert _lib.paged_attention_multi_workspace_bytes(
+        DeviceWorkload(w).k_cache, w.num_seqs, w.num_q_heads, w.max_query_len, w.max_context_len) == 0
+    _run(w, "prefill path, ranked")
+
+
+@pytest.mark.parametrize("dtype,D,bs", [("f16", 64, 32), ("f32", 128, 16)])
+def test_prefill_path_more_than_ranked_sequences(dtype, D, bs):
+    """300 sequences: past the ranking limit, dispatched in index order."""
+    rng = np.random.default_rng(49)
+    ctx = rng.integers(1, 90, size=300)
+    ctx[7] = max(int(ctx[7]), 20)
+    ql = np.minimum(rng.integers(0, 22, size=300), ctx)
+    ql[7] = 20
+    w = wl.build(f"pf_many_{dtype}", 49, rng, ctx, 4, 1, D, bs, dtype, poison=True, query_lens=ql)
+    assert w.max_query_len * 4 >= 64
+    _run(w, f"prefill path, 300 sequences {dtype}")
+
+
+def test_prefill_path_permutation_invariance_bitwise():
+    rng = np.random.default_rng(50)
+    w = wl.build("pfperm", 50, rng, [20, 600, 1500], 32, 8, 128, 16, "bf16",
+                  query_lens=[20, 32, 32])
+    assert w.max_query_len * 4 >= 64
+    base = to_host(DeviceWorkload(w).step(), "bf16")
+    dw = DeviceWorkload(w)
+    dw.write_step()
+    kc, vc = to_host(dw.k_cache, "bf16"), to_host(dw.v_cache, "bf16")
+    pi = np.random.default_rng(51).permutation(kc.shape[0])
+    kp, vp = np.empty_like(kc), np.empty_like(vc)
+    kp[pi], vp[pi] = kc, vc
+    bt = np.where(w.block_tables >= 0, pi[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
+    w2 = wl.Workload(name="pfperm2", dtype="bf16", seed=0, q=w.q, k_cache=kp, v_cache=vp,
+                     block_tables=bt, context_lens=w.context_lens, scale=w.scale,
+                     block_mapping=np.zeros((0, 2), np.int32), slot_mapping=np.zeros((0,), np.int32),
+                     new_key=w.new_key[:0], new_value=w.new_value[:0], query_start=w.query_start)
+    moved = to_host(DeviceWorkload(w2).step(), "bf16")
+    assert np.array_equal(base, moved)
