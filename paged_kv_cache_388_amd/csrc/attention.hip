@@ -333,6 +333,95 @@ __device__ __forceinline__ void attend_core(const uint4 (&ka)[N], const uint32_t
   }
 }
 
+// Two 16-token sub-tiles at once (16-bit types): QK as two independent MFMA
+// chains, one online-softmax update over the 32 tokens, and PV on
+// 16x16x32 MFMAs whose K index runs over both sub-tiles.  The K order is a
+// fixed permutation of the 32 tokens: lane group r holds k = 8r .. 8r+7,
+// taken as tokens 4r .. 4r+3 of the first sub-tile, then of the second.
+// That is exactly what each lane already holds of P (its QK outputs) and of
+// V (its loaded rows), so neither operand is moved between lanes; A and B
+// only need to agree on it.
+template <int DT, int N, int kMM>
+__device__ __forceinline__ void attend_pair(const uint4 (&ka0)[N], const uint4 (&ka1)[N],
+                                            const uint32_t (&v0)[4][N],
+                                            const uint32_t (&v1)[4][N], const uint4 (&qb)[N],
+                                            int valid0, int valid1, float scale_log2, int r,
+                                            WaveState<kMM>& st) {
+  static_assert(DT != DT_F32, "16-bit types only");
+  floatx4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < N; ++kk) {
+    if constexpr (DT == DT_F16) {
+      S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, ka0[kk]),
+                                                  __builtin_bit_cast(halfx8, qb[kk]), S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, ka1[kk]),
+                                                  __builtin_bit_cast(halfx8, qb[kk]), S1, 0, 0, 0);
+    } else {
+      S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka0[kk]),
+                                                   __builtin_bit_cast(bf16x8, qb[kk]), S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka1[kk]),
+                                                   __builtin_bit_cast(bf16x8, qb[kk]), S1, 0, 0, 0);
+    }
+  }
+  float sv[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    sv[e] = (4 * r + e < valid0) ? S0[e] * scale_log2 : kNegInf;
+    sv[4 + e] = (4 * r + e < valid1) ? S1[e] * scale_log2 : kNegInf;
+  }
+  float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  const float m_new = fmaxf(st.m, mloc);
+  const float mb = m_new == kNegInf ? 0.f : m_new;
+  const float alpha = fast_exp2(st.m - mb);
+  float pe[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(sv[e] - mb);
+  st.l = st.l * alpha + (((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7])));
+  st.m = m_new;
+#pragma unroll
+  for (int mm = 0; mm < kMM; ++mm) st.acc[mm] *= alpha;
+
+  uint4 phi, plo;
+  uint32_t* ph = reinterpret_cast<uint32_t*>(&phi);
+  uint32_t* pl = reinterpret_cast<uint32_t*>(&plo);
+#pragma unroll
+  for (int q2 = 0; q2 < 4; ++q2) {
+    const float p0 = pe[2 * q2], p1 = pe[2 * q2 + 1];
+    if constexpr (DT == DT_BF16) {
+      const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
+      ph[q2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+      const floatx2 lo = {p0 - __uint_as_float(b0 & 0xffff0000u), p1 - __uint_as_float(b1 & 0xffff0000u)};
+      pl[q2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+    } else {
+      const fp16x2 hh = __builtin_amdgcn_cvt_pkrtz(p0, p1);
+      ph[q2] = __builtin_bit_cast(uint32_t, hh);
+      pl[q2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p0 - (float)hh[0], p1 - (float)hh[1]));
+    }
+  }
+#pragma unroll
+  for (int mm = 0; mm < kMM; ++mm) {
+    const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
+    const int wd = mm >> 1;
+    uint4 a;
+    a.x = __builtin_amdgcn_perm(v0[1][wd], v0[0][wd], sel);
+    a.y = __builtin_amdgcn_perm(v0[3][wd], v0[2][wd], sel);
+    a.z = __builtin_amdgcn_perm(v1[1][wd], v1[0][wd], sel);
+    a.w = __builtin_amdgcn_perm(v1[3][wd], v1[2][wd], sel);
+    if constexpr (DT == DT_BF16) {
+      const bf16x8 A = __builtin_bit_cast(bf16x8, a);
+      st.acc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, phi), st.acc[mm], 0, 0, 0);
+      st.acc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, plo), st.acc[mm], 0, 0, 0);
+    } else {
+      const halfx8 A = __builtin_bit_cast(halfx8, a);
+      st.acc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(halfx8, phi), st.acc[mm], 0, 0, 0);
+      st.acc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(halfx8, plo), st.acc[mm], 0, 0, 0);
+    }
+  }
+}
+
 // attend_core for a sub-tile as loaded: K is re-dealt through `lds`, this
 // wave's private staging slot (at least one sub-tile of K).
 template <int DT, int N, int kMM>
@@ -1201,30 +1290,54 @@ void attn_prefill_kernel(AttnParams prm) {
   st.reset();
   const float scale_log2 = prm.scale_log2;
   // QK, softmax and PV over the four sub-tiles of stage sg (LDS buffer b).
+  auto fetch = [&](uint4 (&ka)[N], uint32_t (&vv)[4][N], int b, int j) {
+    const int tr = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < N; ++kk) {
+      const int c = (lane >> 4) + 4 * kk;
+      ka[kk] = *reinterpret_cast<const uint4*>(&sK[b][j][tr * kRow + ((c ^ (tr & kSwz)) * 16)]);
+    }
+#pragma unroll
+    for (int qd = 0; qd < N; ++qd) {
+      const uint4 x = *reinterpret_cast<const uint4*>(&sV[b][j][(qd * 64 + lane) * 16]);
+      vv[0][qd] = x.x;
+      vv[1][qd] = x.y;
+      vv[2][qd] = x.z;
+      vv[3][qd] = x.w;
+    }
+  };
+  auto valid_of = [&](int sub) {
+    const int v = vis - sub * kSub;
+    return v > kSub ? kSub : v;
+  };
+  // QK, softmax and PV over the four sub-tiles of stage sg (LDS buffer b):
+  // two pairs for 16-bit types (a pair whose second sub-tile is past this
+  // wave's limit masks it: every token there is past every column's limit),
+  // four single sub-tiles for fp32.
   auto compute_stage = [&](int sg, int b) {
+    if constexpr (DT != DT_F32) {
 #pragma unroll
-    for (int j = 0; j < kWaves; ++j) {
-      const int sub = sg * kWaves + j;
-      if (sub < nsub_w) {
-        uint4 ka[N];
-        uint32_t vv[4][N];
-        const int tr = lane & 15;
-#pragma unroll
-        for (int kk = 0; kk < N; ++kk) {
-          const int c = (lane >> 4) + 4 * kk;
-          ka[kk] = *reinterpret_cast<const uint4*>(&sK[b][j][tr * kRow + ((c ^ (tr & kSwz)) * 16)]);
+      for (int j = 0; j < kWaves; j += 2) {
+        const int sub = sg * kWaves + j;
+        if (sub < nsub_w) {
+          uint4 ka0[N], ka1[N];
+          uint32_t v0[4][N], v1[4][N];
+          fetch(ka0, v0, b, j);
+          fetch(ka1, v1, b, j + 1);
+          attend_pair<DT, N, kMM>(ka0, ka1, v0, v1, qb, valid_of(sub), valid_of(sub + 1),
+                                  scale_log2, r, st);
         }
+      }
+    } else {
 #pragma unroll
-        for (int qd = 0; qd < N; ++qd) {
-          const uint4 x = *reinterpret_cast<const uint4*>(&sV[b][j][(qd * 64 + lane) * 16]);
-          vv[0][qd] = x.x;
-          vv[1][qd] = x.y;
-          vv[2][qd] = x.z;
-          vv[3][qd] = x.w;
+      for (int j = 0; j < kWaves; ++j) {
+        const int sub = sg * kWaves + j;
+        if (sub < nsub_w) {
+          uint4 ka[N];
+          uint32_t vv[4][N];
+          fetch(ka, vv, b, j);
+          attend_core<DT, N, kMM>(ka, vv, qb, valid_of(sub), scale_log2, r, st);
         }
-        int valid = vis - sub * kSub;
-        valid = valid > kSub ? kSub : valid;
-        attend_core<DT, N, kMM>(ka, vv, qb, valid, scale_log2, r, st);
       }
     }
   };
