@@ -1,0 +1,63 @@
+"""The device entry points under HIP graph capture (needs an MI355X).
+
+A serving loop replays one captured step per token instead of launching each
+kernel.  The entry points allocate nothing, set no memory and never
+synchronise, so a step of paged_copy_blocks + paged_kv_append + attention is
+captured as is; each replay must give exactly the eager result.  Replays are
+interleaved with eager work on the same buffers and with synchronisations,
+and every replay is checked, not only the first.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_388_amd import _lib
+from paged_kv_cache_388_amd import workloads as wl
+
+from gpu_common import DeviceWorkload, check_attention, oracle_step, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _graph_vs_eager(w, what):
+    print(f"[gpu] graph {what}: B={w.num_seqs} multi={w.multi}", flush=True)
+    dw = DeviceWorkload(w)
+    eager = to_host(dw.step(), w.dtype)       # also caches the device's grid size
+    torch.cuda.synchronize()
+    check_attention(eager, oracle_step(w), w.dtype, what)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dw.step()                              # warm-up on the side stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        captured = dw.step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        captured.zero_()
+        dw.step()                              # eager work on the same buffers between replays
+        torch.cuda.synchronize()
+        captured.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        got = to_host(captured, w.dtype)
+        assert np.array_equal(got.view(np.uint8), eager.view(np.uint8)), f"{what}: replay {rep}"
+
+
+def test_graph_decode_stream_path():
+    rng = np.random.default_rng(61)
+    w = wl.build("g_dec", 61, rng, rng.integers(1, 3000, size=48), 32, 8, 128, 16, "bf16",
+                 poison=True)
+    _graph_vs_eager(w, "decode")
+
+
+def test_graph_multi_stream_and_prefill_paths():
+    rng = np.random.default_rng(62)
+    ctx = [40, 900, 1700, 33]
+    w = wl.build("g_spec", 62, rng, ctx, 32, 8, 128, 16, "bf16", query_lens=[4, 4, 4, 4])
+    _graph_vs_eager(w, "multi, stream path")
+    w = wl.build("g_pf", 63, rng, ctx, 32, 8, 128, 16, "bf16", query_lens=[33, 64, 20, 33])
+    _graph_vs_eager(w, "multi, prefill path")
