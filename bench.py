@@ -100,29 +100,42 @@ def cpu_baseline(w, min_seconds):
             kc, vc = oracle.kv_append(kc, vc, w.new_key, w.new_value, w.slot_mapping)
         t1 = time.perf_counter()
         seqs = 0
+        rows = 0
         kv = 0
         while True:
             for s in range(w.num_seqs):
                 if w.multi:
+                    # the sequence's new rows in slices of up to 16: a slice of
+                    # rows [a, e) is the last e - a tokens of a context of
+                    # n - L + e tokens, which is what each of its rows sees
                     r0, r1 = int(w.query_start[s]), int(w.query_start[s + 1])
-                    oracle.multi_query_attention(w.q[r0:r1], kc, vc, w.block_tables[s:s + 1],
-                                                 w.context_lens[s:s + 1], [r1 - r0], w.scale,
-                                                 w.dtype)
+                    n, L = int(w.context_lens[s]), r1 - r0
+                    for a in range(0, L, 16):
+                        e = min(a + 16, L)
+                        oracle.multi_query_attention(
+                            w.q[r0 + a:r0 + e], kc, vc, w.block_tables[s:s + 1],
+                            np.array([n - L + e], dtype=np.int32), [e - a], w.scale, w.dtype)
+                        kv += 2 * (n - L + e) * w.num_kv_heads * w.head_dim * b
+                        rows += e - a
+                        if time.perf_counter() - t1 > min_seconds:
+                            break
                 else:
                     oracle.decode_attention(w.q, kc, vc, w.block_tables, w.context_lens,
                                             w.scale, w.dtype, seq_ids=[s])
+                    kv += 2 * int(w.context_lens[s]) * w.num_kv_heads * w.head_dim * b
+                    rows += 1
                 seqs += 1
-                kv += 2 * int(w.context_lens[s]) * w.num_kv_heads * w.head_dim * b
                 if time.perf_counter() - t1 > min_seconds:
                     break
             if time.perf_counter() - t1 > min_seconds:
                 break
         dt = time.perf_counter() - t1
     return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{seqs} sequence-attentions of this step ({seqs / w.num_seqs:.2f} passes "
-                       f"over the {w.num_seqs}-sequence batch) after its cache writes "
+            "sample": (f"{rows} query rows of {seqs} sequence-attentions of this step "
+                       f"({seqs / w.num_seqs:.2f} passes over the {w.num_seqs}-sequence batch, "
+                       f"the last one possibly in part) after its cache writes "
                        f"({t1 - t0:.1f} s), fp64 NumPy, one thread, {dt:.1f} s"),
-            "seqs_per_s": round(seqs / dt, 2)}
+            "rows_per_s": round(rows / dt, 2)}
 
 
 def block_manager_trace(seed=388008, num_seqs=256, system_tokens=1000, steps=256):

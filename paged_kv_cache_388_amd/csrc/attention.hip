@@ -1158,10 +1158,12 @@ __global__ __launch_bounds__(64) void attn_stream_merge_kernel(AttnParams prm) {
 // (the block table row read with scalar loads), parks it in LDS (K in the
 // A-operand staging order, V in its load order), and after a barrier every
 // wave runs QK, online softmax and PV over the stage's four sub-tiles for its
-// own 16 columns.  The next three stages' loads are in flight meanwhile.  The
-// workgroup covers the whole context, so it writes the output rows directly.
-// Grid: column block x kv head x sequence rank; blocks past a sequence's
-// columns exit at once.
+// own 16 columns.  The next three stages' loads are in flight meanwhile.  A
+// workgroup that covers the whole context writes the output rows directly;
+// when a call has too few workgroups to fill the chip, each context is cut
+// into stage-aligned parts, one workgroup each, and a merge combines the
+// parts' states.  Grid: (column block, part) x kv head x sequence rank;
+// blocks past a sequence's columns, and empty parts, exit at once.
 
 template <int DT, int D, int BS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
@@ -1180,7 +1182,9 @@ void attn_prefill_kernel(AttnParams prm) {
   const int w = uniform(tid >> 6);
   const int r = lane >> 4;
   const int h = (int)blockIdx.y;
-  const int cb = (int)blockIdx.x;
+  const int P = prm.prefill_parts;
+  const int cb = (int)blockIdx.x / P;
+  const int part = (int)blockIdx.x % P;
   const int G = prm.group;
   const int Hq = prm.num_q_heads;
 
@@ -1242,7 +1246,13 @@ void attn_prefill_kernel(AttnParams prm) {
   const int cg_last = (cb + 1) * kWaves < ngrp ? (cb + 1) * kWaves - 1 : ngrp - 1;
   const int rows_b = group_limit(cg_last);
   const int nsub_b = (rows_b + kSub - 1) / kSub;
-  const int nstage = (nsub_b + kWaves - 1) / kWaves;
+  const int nstage_all = (nsub_b + kWaves - 1) / kWaves;
+  // this workgroup's part of the context: stages [st0, st1)
+  const int per_part = (nstage_all + P - 1) / P;
+  const int st0 = part * per_part;
+  const int st1 = st0 + per_part < nstage_all ? st0 + per_part : nstage_all;
+  if (st0 >= st1) return;  // an empty part: the merge skips it
+  const int sub_end = st1 * kWaves < nsub_b ? st1 * kWaves : nsub_b;
 
   typedef const __attribute__((address_space(4))) int32_t const_i32;
   const_i32* row_ids = (const_i32*)prm.block_tables + (size_t)s * prm.max_blocks_per_seq;
@@ -1255,7 +1265,7 @@ void attn_prefill_kernel(AttnParams prm) {
     const char* kb = static_cast<const char*>(prm.k_cache);
     const char* vb = static_cast<const char*>(prm.v_cache);
     int nrec = 0;
-    if (sub < nsub_b) {
+    if (sub < sub_end) {
       const int blk = sub * kSub / BS;  // < ceil(rows_b / BS) <= max_blocks_per_seq
       int phys = row_ids[blk];
       const bool ok = (unsigned)phys < (unsigned)prm.num_blocks;
@@ -1346,26 +1356,27 @@ void attn_prefill_kernel(AttnParams prm) {
   // stage sg is computed from LDS, and stage sg + 1 is parked in the other
   // buffer (whose last readers finished before the previous barrier).
   Tile<N> t0, t1, t2;
-  load_sub(t0, w);
-  load_sub(t1, kWaves + w);
-  load_sub(t2, 2 * kWaves + w);
+  load_sub(t0, st0 * kWaves + w);
+  load_sub(t1, (st0 + 1) * kWaves + w);
+  load_sub(t2, (st0 + 2) * kWaves + w);
   park(t0, 0);
   __syncthreads();
   // Rounds of three stages with no exit in between: every path issues the
   // same loads, so each park waits for its own tile only.  Stages past the
-  // end load nothing and compute nothing.
-  for (int sg = 0; sg < nstage; sg += 3) {
+  // part load nothing and compute nothing.
+  for (int sg = st0; sg < st1; sg += 3) {
+    const int b = (sg - st0) & 1;
     load_sub(t0, (sg + 3) * kWaves + w);
-    compute_stage(sg, sg & 1);
-    park(t1, (sg + 1) & 1);
+    compute_stage(sg, b);
+    park(t1, b ^ 1);
     __syncthreads();
     load_sub(t1, (sg + 4) * kWaves + w);
-    if (sg + 1 < nstage) compute_stage(sg + 1, (sg + 1) & 1);
-    park(t2, (sg + 2) & 1);
+    if (sg + 1 < st1) compute_stage(sg + 1, b ^ 1);
+    park(t2, b);
     __syncthreads();
     load_sub(t2, (sg + 5) * kWaves + w);
-    if (sg + 2 < nstage) compute_stage(sg + 2, (sg + 2) & 1);
-    park(t0, (sg + 3) & 1);
+    if (sg + 2 < st1) compute_stage(sg + 2, b);
+    park(t0, b ^ 1);
     __syncthreads();
   }
 
@@ -1376,12 +1387,80 @@ void attn_prefill_kernel(AttnParams prm) {
     lane_run<D, kMM>(o, st);
     if (col < L * G) {
       const size_t orow = (size_t)(q0 + col / G) * Hq + (size_t)h * G + col % G;
-      const float inv = l > 0.f ? 1.f / l : 0.f;
+      if (P == 1) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-      for (int i = 0; i < D / 4; ++i) o[i] *= inv;
-      store_run<DT, D>(static_cast<char*>(prm.out) + (orow * D + r * (D / 4)) * Geo::EB, o);
+        for (int i = 0; i < D / 4; ++i) o[i] *= inv;
+        store_run<DT, D>(static_cast<char*>(prm.out) + (orow * D + r * (D / 4)) * Geo::EB, o);
+      } else {
+        // part state: unnormalised o, running max (log2 units), normaliser
+        const size_t slot = orow * P + part;
+        store_run<DT_F32, D>(prm.part_o + slot * D + r * (D / 4), o);
+        if (r == 0) *reinterpret_cast<float2*>(prm.part_ml + slot * 2) = make_float2(st.m, l);
+      }
     }
   }
+}
+
+// Merge of a split prefill context for one (query row, query head): one
+// wave, lanes over the head dim, parts in order.  Grid: sequence x new token
+// (up to max_query_len) x query head, a wave each, four per workgroup.  The
+// number of non-empty parts follows from the same stage counts the prefill
+// kernel uses.
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void attn_prefill_merge_kernel(AttnParams prm) {
+  const int lane = threadIdx.x & 63;
+  const long long id = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int Hq = prm.num_q_heads;
+  const int G = prm.group;
+  const int P = prm.prefill_parts;
+  const int hq = (int)(id % Hq);
+  const long long rest = id / Hq;
+  const int i = (int)(rest % prm.max_query_len);
+  const int s = (int)(rest / prm.max_query_len);
+  if (s >= prm.num_seqs) return;
+  int n = prm.context_lens[s];
+  n = n < 0 ? 0 : (n > prm.max_context_len ? prm.max_context_len : n);
+  const int T = prm.num_query_tokens;
+  int q0 = prm.query_start[s], qe = prm.query_start[s + 1];
+  q0 = q0 < 0 ? 0 : (q0 > T ? T : q0);
+  qe = qe < q0 ? q0 : (qe > T ? T : qe);
+  int L = qe - q0;
+  L = L < n ? L : n;
+  L = L < prm.max_query_len ? L : prm.max_query_len;
+  if (i >= L) return;
+  const int c = i * G + hq % G;  // the column, in its kv head's block
+  const int cb = c / (kWaves * kSub);
+  const int ngrp = (L * G + kSub - 1) / kSub;
+  const int cg_last = (cb + 1) * kWaves < ngrp ? (cb + 1) * kWaves - 1 : ngrp - 1;
+  int i_last = (cg_last * kSub + kSub - 1) / G;
+  i_last = i_last < L - 1 ? i_last : L - 1;
+  const int rows_b = n - L + i_last + 1;
+  const int nstage_all = ((rows_b + kSub - 1) / kSub + kWaves - 1) / kWaves;
+  const int per_part = (nstage_all + P - 1) / P;
+  const int nparts = (nstage_all + per_part - 1) / per_part;
+  const size_t base = ((size_t)(q0 + i) * Hq + hq) * P;
+  constexpr int kPer = D / 64;
+
+  float M = kNegInf;
+  for (int k = lane; k < nparts; k += 64) M = fmaxf(M, prm.part_ml[(base + k) * 2]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float o[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) o[j] = 0.f;
+  float lsum = 0.f;
+  for (int k = 0; k < nparts; ++k) {
+    const float2 ml = *reinterpret_cast<const float2*>(prm.part_ml + (base + k) * 2);
+    const float f = ml.x == kNegInf ? 0.f : fast_exp2(ml.x - M);
+    lsum += f * ml.y;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) o[j] += f * prm.part_o[(base + k) * D + lane + 64 * j];
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const size_t orow = ((size_t)(q0 + i) * Hq + hq) * D;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) store_out<DT>(prm.out, orow + lane + 64 * j, o[j] * inv);
 }
 
 template <int DT, int D, int BS>
@@ -1390,12 +1469,20 @@ hipError_t launch_typed(const AttnParams& prm, hipStream_t stream) {
   const long long nout = (long long)prm.num_seqs * prm.num_q_heads;
   if (nout > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (prm.prefill_blocks > 0) {
-    if (!prm.query_start || prm.num_seqs > 65535 || prm.num_kv_heads > 65535)
+    const long long nx = (long long)prm.prefill_blocks * prm.prefill_parts;
+    if (!prm.query_start || prm.num_seqs > 65535 || prm.num_kv_heads > 65535 ||
+        prm.prefill_parts < 1 || nx > 0x7fffffffLL)
       return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((attn_prefill_kernel<DT, D, BS>),
-                       dim3((unsigned)prm.prefill_blocks, (unsigned)prm.num_kv_heads,
-                            (unsigned)prm.num_seqs),
+                       dim3((unsigned)nx, (unsigned)prm.num_kv_heads, (unsigned)prm.num_seqs),
                        block, 0, stream, prm);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || prm.prefill_parts == 1) return err;
+    const long long waves = (long long)prm.num_seqs * prm.max_query_len * prm.num_q_heads;
+    const long long nm = (waves + kWaves - 1) / kWaves;
+    if (nm > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((attn_prefill_merge_kernel<DT, D>), dim3((unsigned)nm), block, 0, stream,
+                       prm);
     return hipGetLastError();
   }
   if (prm.stream_wgs > 0) {
@@ -1471,6 +1558,28 @@ AttnWorkspace attn_workspace_layout(int32_t num_seqs, int32_t slot_cols, int32_t
   ws.part_o_off = 0;
   ws.part_ml_off = rows * head_dim * sizeof(float);
   ws.bytes = ws.part_ml_off + rows * 2 * sizeof(float);
+  return ws;
+}
+
+int32_t prefill_parts_for(int32_t num_seqs, int32_t num_kv_heads, int32_t prefill_blocks,
+                          int32_t max_context_len) {
+  const long long wgs = (long long)num_seqs * num_kv_heads * prefill_blocks;
+  if (wgs <= 0 || wgs >= kPrefillMinWorkgroups) return 1;
+  long long p = (kPrefillMinWorkgroups + wgs - 1) / wgs;
+  const long long by_len = max_context_len / kPrefillMinPartTokens;
+  if (p > by_len) p = by_len;
+  if (p > kPrefillMaxParts) p = kPrefillMaxParts;
+  return p < 1 ? 1 : (int32_t)p;
+}
+
+AttnWorkspace prefill_workspace_layout(int32_t num_query_tokens, int32_t num_q_heads,
+                                       int32_t head_dim, int32_t parts) {
+  AttnWorkspace ws{0, 0, 0, 0};
+  if (parts <= 1 || num_query_tokens <= 0 || num_q_heads <= 0 || head_dim <= 0) return ws;
+  const size_t slots = (size_t)num_query_tokens * num_q_heads * parts;
+  ws.part_o_off = 0;
+  ws.part_ml_off = align256(slots * head_dim * sizeof(float));
+  ws.bytes = ws.part_ml_off + slots * 2 * sizeof(float);
   return ws;
 }
 

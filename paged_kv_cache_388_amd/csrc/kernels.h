@@ -29,6 +29,12 @@ constexpr int kPrefillMinCols = 64;
 // Up to this many sequences the prefill path dispatches them longest context
 // first (each workgroup ranks the context lengths itself).
 constexpr int kPrefillRankSeqs = 256;
+// The prefill path splits contexts when a call has fewer than this many
+// (sequence, kv head, column block) workgroups, into at most kPrefillMaxParts
+// parts of at least kPrefillMinPartTokens tokens.
+constexpr int kPrefillMinWorkgroups = 1024;
+constexpr int kPrefillMaxParts = 16;
+constexpr int kPrefillMinPartTokens = 512;
 // Positions (H_kv x sub-tiles of the batch) the stream path indexes in 32 bits;
 // the host sends calls whose bound B * ceil(max_ctx / 16) * H_kv exceeds it to
 // the grid path.
@@ -70,9 +76,14 @@ struct AttnParams {
   int32_t max_query_len;        // host-known bound of the new tokens per sequence
   int32_t max_groups;           // ceil(max_query_len * G / 16)
   int32_t slot_cols;            // columns per partial slot: min(16, max_query_len * G)
-  // > 0: prefill path, this many workgroups per (sequence, kv head), each
-  // taking four 16-column groups (ceil(max_groups / 4)); no workspace.
+  // > 0: prefill path, this many column blocks per (sequence, kv head), each
+  // taking four 16-column groups (ceil(max_groups / 4)).
   int32_t prefill_blocks;
+  // Prefill path: the context of each (sequence, kv head, column block) is
+  // cut into this many stage-aligned parts, one workgroup each.  With more
+  // than one, part states go to part_o [rows * H_q * parts, D] and part_ml
+  // [rows * H_q * parts, 2] (row = query row) and a merge writes `out`.
+  int32_t prefill_parts;
 };
 
 // Workspace layout of one decode call, shared by the size query and the call.
@@ -82,6 +93,12 @@ struct AttnWorkspace {
 // slot_cols: columns per partial slot (min(16, max_query_len * G)).
 AttnWorkspace attn_workspace_layout(int32_t num_seqs, int32_t slot_cols, int32_t num_q_heads,
                                     int32_t head_dim, int32_t max_context_len, int32_t stream_wgs);
+// Prefill path: parts per (sequence, kv head, column block), and the
+// workspace of the part states (0 bytes with one part).
+int32_t prefill_parts_for(int32_t num_seqs, int32_t num_kv_heads, int32_t prefill_blocks,
+                          int32_t max_context_len);
+AttnWorkspace prefill_workspace_layout(int32_t num_query_tokens, int32_t num_q_heads,
+                                       int32_t head_dim, int32_t parts);
 
 // dtype: 0 f32, 1 f16, 2 bf16.  Returns hipErrorInvalidValue for a (dtype,
 // head_dim, block_size) combination that is not instantiated.

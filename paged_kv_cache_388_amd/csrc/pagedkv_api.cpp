@@ -158,7 +158,16 @@ size_t attention_workspace(const pkv_pool& pool, int32_t num_seqs, int32_t num_q
     return 0;
   const int32_t group = num_q_heads / pool.num_kv_heads;
   const int32_t groups = max_groups_for(max_query_len, group);
-  if (multi && prefill_route(max_query_len, group)) return 0;
+  if (multi && prefill_route(max_query_len, group)) {
+    const int32_t blocks = (groups + pkv::kStreamWaves - 1) / pkv::kStreamWaves;
+    const int32_t parts =
+        pkv::prefill_parts_for(num_seqs, pool.num_kv_heads, blocks, max_context_len);
+    // every query row may belong to a split context: bound by the rows the
+    // batch can hold (num_seqs * max_query_len)
+    const long long rows = (long long)num_seqs * max_query_len;
+    if (rows > 0x7fffffffLL) return 0;
+    return pkv::prefill_workspace_layout((int32_t)rows, num_q_heads, pool.head_dim, parts).bytes;
+  }
   const int32_t wgs = stream_wgs_for(num_seqs, pool.num_kv_heads, max_context_len, groups, multi);
   if (multi && wgs == 0) return 0;
   return pkv::attn_workspace_layout(num_seqs, slot_cols_for(max_query_len, group), num_q_heads,
@@ -212,8 +221,11 @@ pkv_status attention_call(const char* what, void* out, const void* q, const void
                 "(kv heads x 16-column groups x 16-token sub-tiles)",
                 pkv::kMaxMultiSeqs);
   const int32_t cols = slot_cols_for(max_query_len, group);
+  const int32_t pf_blocks = prefill ? (groups + pkv::kStreamWaves - 1) / pkv::kStreamWaves : 0;
+  const int32_t pf_parts =
+      prefill ? pkv::prefill_parts_for(num_seqs, pool.num_kv_heads, pf_blocks, max_context_len) : 1;
   const pkv::AttnWorkspace lay =
-      prefill ? pkv::AttnWorkspace{0, 0, 0, 0}
+      prefill ? pkv::prefill_workspace_layout(num_query_tokens, num_q_heads, pool.head_dim, pf_parts)
               : pkv::attn_workspace_layout(num_seqs, cols, num_q_heads, pool.head_dim,
                                            max_context_len, stream_wgs);
   if (lay.bytes > 0 && (!workspace || workspace_bytes < lay.bytes))
@@ -246,7 +258,8 @@ pkv_status attention_call(const char* what, void* out, const void* q, const void
   prm.max_query_len = multi ? max_query_len : 1;
   prm.max_groups = groups;
   prm.slot_cols = cols;
-  prm.prefill_blocks = prefill ? (groups + pkv::kStreamWaves - 1) / pkv::kStreamWaves : 0;
+  prm.prefill_blocks = pf_blocks;
+  prm.prefill_parts = pf_parts;
   hipError_t err = pkv::launch_paged_attention(prm, pool.dtype, pool.head_dim, pool.block_size, stream);
   return err == hipSuccess ? PKV_OK : hip_fail(err, what);
 }

@@ -36,7 +36,7 @@ ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 NAN_BITS = {"f16": 0x7E00, "bf16": 0x7FC0}
 
 NAMED = ("tiny_f32", "llama2_7b_f16", "llama3_8b_gqa", "shared_prefix", "long_ctx")
-MULTI = ("spec_verify", "prefill_chunk")
+MULTI = ("spec_verify", "prefill_chunk", "long_prompt_chunk")
 
 
 @dataclass
@@ -347,6 +347,17 @@ def prefill_chunk(seed=388007, poison=False, num_seqs=8, chunk=256):
                  poison=poison, query_lens=np.full(num_seqs, chunk, dtype=np.int32))
 
 
+def long_prompt_chunk(seed=388010, poison=False, context=32768, chunk=256):
+    """Chunked prefill of one long prompt on the Llama-3-8B-shaped GQA layer:
+    the chunk of ``chunk`` new tokens that ends a ``context``-token prompt
+    (each new token attends to everything before it), bf16.  A single
+    sequence gives the prefill path only 16 x 8 (column block, kv head)
+    workgroups, so its context is cut into parts."""
+    rng = np.random.default_rng(seed)
+    return build("long_prompt_chunk", seed, rng, [context], 32, 8, 128, 16, "bf16",
+                 poison=poison, query_lens=[chunk])
+
+
 def named(name, **kw):
     """Build a named workload: one of NAMED, or ``long_ctx_bs16``/``long_ctx_bs32``."""
     if name == "tiny_f32":
@@ -365,4 +376,6 @@ def named(name, **kw):
         return spec_verify(**kw)
     if name == "prefill_chunk":
         return prefill_chunk(**kw)
+    if name == "long_prompt_chunk":
+        return long_prompt_chunk(**kw)
     raise KeyError(name)

@@ -116,8 +116,13 @@ def test_prefill_path_ranked_ties_and_mixed_lengths():
     ql = [40, 1, 17, 64, 0, 0, 31]
     w = wl.build("pf_mixed", 48, rng, ctx, 8, 2, 128, 16, "bf16", poison=True, query_lens=ql)
     assert w.max_query_len * 4 >= 64
+    # 7 sequences x 2 kv heads x 4 column blocks = 56 workgroups: contexts are
+    # cut in two (1300 // 512 caps the parts), part states for 7 x 64 rows x 8 heads
+    rows, parts, D = 7 * 64, 2, 128
+    want = -(-(rows * 8 * parts * D * 4) // 256) * 256 + rows * 8 * parts * 2 * 4
     assert _lib.paged_attention_multi_workspace_bytes(
-        DeviceWorkload(w).k_cache, w.num_seqs, w.num_q_heads, w.max_query_len, w.max_context_len) == 0
+        DeviceWorkload(w).k_cache, w.num_seqs, w.num_q_heads, w.max_query_len,
+        w.max_context_len) == want
     _run(w, "prefill path, ranked")
 
 
@@ -153,3 +158,42 @@ def test_prefill_path_permutation_invariance_bitwise():
                      new_key=w.new_key[:0], new_value=w.new_value[:0], query_start=w.query_start)
     moved = to_host(DeviceWorkload(w2).step(), "bf16")
     assert np.array_equal(base, moved)
+
+
+@pytest.mark.parametrize("ctx,ql,hq,hkv,dtype", [
+    ([5000], [64], 8, 2, "bf16"),                 # one long prompt: 8 workgroups, cut into 9 parts
+    ([3000, 700], [100, 40], 8, 1, "f16"),        # G = 8, parts per sequence differ
+    ([2500, 1], [256, 1], 4, 4, "bf16"),          # G = 1, a 256-token chunk
+])
+def test_prefill_path_split_context(ctx, ql, hq, hkv, dtype):
+    """Too few workgroups to fill the chip: each context is cut into parts,
+    one workgroup each, and a merge combines their states."""
+    rng = np.random.default_rng(52)
+    w = wl.build(f"pf_split_{len(ctx)}_{dtype}", 52, rng, ctx, hq, hkv, 128, 16, dtype,
+                 poison=True, query_lens=ql)
+    G = hq // hkv
+    assert w.max_query_len * G >= 64
+    dw = DeviceWorkload(w)
+    assert _lib.paged_attention_multi_workspace_bytes(
+        dw.k_cache, w.num_seqs, w.num_q_heads, w.max_query_len, w.max_context_len) > 0
+    _run(w, f"prefill path, split contexts {ctx}")
+
+
+def test_long_prompt_chunk_sampled_rows():
+    """The full-size one-long-prompt chunk (256 new tokens ending a
+    32768-token context; its context is cut into parts).  Sampled rows are
+    checked against decode attention over the tokens each row may see, the
+    form the multi-token oracle reduces to row by row."""
+    import oracle
+    from gpu_common import oracle_pools_after_step
+    w = wl.named("long_prompt_chunk")
+    print(f"[gpu] long_prompt_chunk: n={w.max_context_len} L={w.max_query_len}", flush=True)
+    dw = DeviceWorkload(w)
+    out = to_host(dw.step(), w.dtype)
+    torch.cuda.synchronize()
+    kc, vc = oracle_pools_after_step(w)
+    n, L = int(w.context_lens[0]), int(w.max_query_len)
+    rows = np.array([0, 1, 63, 64, 127, 200, 254, 255])
+    ref = oracle.decode_attention(w.q[rows], kc, vc, np.repeat(w.block_tables[:1], len(rows), 0),
+                                  (n - L + rows + 1).astype(np.int32), w.scale, w.dtype)
+    check_attention(out[rows], ref, w.dtype, "long_prompt_chunk sampled rows")
