@@ -50,6 +50,21 @@ def algorithmic_bytes(w):
             + 4 * w.num_seqs + extra)
 
 
+def unique_kv_bytes(w):
+    """Bytes of K and V held by the distinct physical blocks the batch reads
+    (each block counted up to the most tokens any sequence reads from it):
+    the traffic floor when blocks are shared.  Equal to kv_bytes() without
+    sharing."""
+    b = wl.ELEM_BYTES[w.dtype]
+    fill = {}
+    for s in range(w.num_seqs):
+        n = int(w.context_lens[s])
+        for j in range((n + w.block_size - 1) // w.block_size):
+            blk = int(w.block_tables[s, j])
+            fill[blk] = max(fill.get(blk, 0), min(w.block_size, n - j * w.block_size))
+    return 2 * sum(fill.values()) * w.num_kv_heads * w.head_dim * b
+
+
 def attention_flops(w):
     """QK and PV multiply-adds of one call: 4 * D flops per (new token, query
     head, visible context token)."""
@@ -387,6 +402,9 @@ def main():
     ap.add_argument("--read-probe-mib", type=int, default=0,
                     help="instead of the decode step, time pkv_stream_read of this many MiB "
                          "(the achievable read-bandwidth reference)")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 1 GiB scrub buffer before every timed step, so that no "
+                         "K/V byte is served from L2 or the Infinity Cache")
     ap.add_argument("--swap", action="store_true",
                     help="instead of the decode step, time swap out / in of a preempted batch")
     ap.add_argument("--block-manager", action="store_true",
@@ -476,24 +494,54 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+    scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold else None
+    wstarts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if scrub is not None:
+            scrub.fill_(i & 0xff)
+        wstarts[i].record(stream)
         write_step()
         starts[i].record(stream)
         attend()
         ends[i].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    write_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(wstarts, starts)]))
+
+    # the achievable-read reference on the same device: 4 GiB read once
+    probe_src = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    probe_sink = torch.zeros(_lib.STREAM_READ_WORKGROUPS, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        _lib.pkv_stream_read(probe_src, probe_sink)
+    pa = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    pb = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    for i in range(5):
+        pa[i].record(stream)
+        _lib.pkv_stream_read(probe_src, probe_sink)
+        pb[i].record(stream)
+    torch.cuda.synchronize()
+    probe_gbs = (4 << 30) / (float(np.mean([a.elapsed_time(b) for a, b in zip(pa, pb)])) * 1e-3) / 1e9
+    del probe_src
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     attn_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     attn_avg_ms = float(np.mean(attn_ms))
+    if args.cold:
+        # the scrub is not part of the step: take the step from its events
+        ms_per_step = write_ms + attn_avg_ms
     kv = w.kv_bytes()
     value = kv / (ms_per_step * 1e-3) / 1e9
     alg = algorithmic_bytes(w)
+    uniq = unique_kv_bytes(w)
+    shared = uniq < kv
+    if shared:
+        # blocks shared between sequences are read once from HBM at best:
+        # the roofline is taken on the distinct bytes
+        alg = alg - kv + uniq
     achieved = alg / (attn_avg_ms * 1e-3) / 1e9
     line = {
         "metric": METRIC,
@@ -516,11 +564,14 @@ def main():
                    "step": ("copy_blocks + paged_kv_append + "
                             + ("paged_attention_multi" if w.multi else "paged_attention_decode")),
                    "new_tokens": int(w.q.shape[0]),
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "cold": bool(args.cold)},
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "seqs_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "new_tokens_per_s": round(w.q.shape[0] / (ms_per_step * 1e-3), 1),
         "attention_tflops": round(attention_flops(w) / (attn_avg_ms * 1e-3) / 1e12, 2),
+        "cache_writes_ms": round(write_ms, 4),
+        "read_probe_GBps": round(probe_gbs, 1),
+        "frac_of_read_probe": round(achieved / probe_gbs, 4),
         "attention_ms": {"mean": round(attn_avg_ms, 4),
                          "p10": round(float(np.percentile(attn_ms, 10)), 4),
                          "p50": round(float(np.percentile(attn_ms, 50)), 4),
@@ -532,7 +583,12 @@ def main():
                                 "attn_stream_merge_kernel (one "
                                 f"{'paged_attention_multi' if w.multi else 'paged_attention_decode'}"
                                 " call)"),
-                     "algorithmic_bytes_per_launch": alg},
+                     "algorithmic_bytes_per_launch": alg,
+                     **({"kv_bytes_logical": kv, "kv_bytes_unique": uniq,
+                         "note": ("K/V shared between sequences: achieved counts each distinct "
+                                  "byte once; the distinct footprint fits in the Infinity "
+                                  "Cache, so a warm run is not HBM-bound (see --cold)")}
+                        if shared else {})},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
