@@ -338,15 +338,23 @@ __device__ __forceinline__ void attend_core(const uint4 (&ka)[N], const uint32_t
 // 16x16x32 MFMAs whose K index runs over both sub-tiles.  The K order is a
 // fixed permutation of the 32 tokens: lane group r holds k = 8r .. 8r+7,
 // taken as tokens 4r .. 4r+3 of the first sub-tile, then of the second.
-// That is exactly what each lane already holds of P (its QK outputs) and of
-// V (its loaded rows), so neither operand is moved between lanes; A and B
-// only need to agree on it.
-template <int DT, int N, int kMM>
+// That is exactly what each lane holds of P (its QK outputs) and of V (its
+// loaded rows), so no operand moves between lanes; A and B only need to
+// agree on it.  V comes pre-arranged (va[wd] = the four A-operand words of
+// head-dim pair wd: rows 0-1 and 2-3 of the even dim, then of the odd one).
+//
+// The softmax reference max is updated lazily: a column keeps its reference
+// m while its new logits stay within kLazyLog2 of it (its p stay <= 2^8), and
+// the accumulators are rescaled only when some column of the wave moves its
+// reference.  o = acc / l holds for any reference, so this changes rounding
+// only.  MASK = false when every real column sees all 32 tokens.
+constexpr float kLazyLog2 = 8.f;
+
+template <int DT, int N, int kMM, bool MASK>
 __device__ __forceinline__ void attend_pair(const uint4 (&ka0)[N], const uint4 (&ka1)[N],
-                                            const uint32_t (&v0)[4][N],
-                                            const uint32_t (&v1)[4][N], const uint4 (&qb)[N],
-                                            int valid0, int valid1, float scale_log2, int r,
-                                            WaveState<kMM>& st) {
+                                            const u32x4 (&va0)[N], const u32x4 (&va1)[N],
+                                            const uint4 (&qb)[N], int valid0, int valid1,
+                                            float scale_log2, int r, WaveState<kMM>& st) {
   static_assert(DT != DT_F32, "16-bit types only");
   floatx4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -366,23 +374,31 @@ __device__ __forceinline__ void attend_pair(const uint4 (&ka0)[N], const uint4 (
   float sv[8];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    sv[e] = (4 * r + e < valid0) ? S0[e] * scale_log2 : kNegInf;
-    sv[4 + e] = (4 * r + e < valid1) ? S1[e] * scale_log2 : kNegInf;
+    sv[e] = S0[e] * scale_log2;
+    sv[4 + e] = S1[e] * scale_log2;
+    if constexpr (MASK) {
+      sv[e] = (4 * r + e < valid0) ? sv[e] : kNegInf;
+      sv[4 + e] = (4 * r + e < valid1) ? sv[4 + e] : kNegInf;
+    }
   }
   float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
   mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
   mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-  const float m_new = fmaxf(st.m, mloc);
-  const float mb = m_new == kNegInf ? 0.f : m_new;
-  const float alpha = fast_exp2(st.m - mb);
+  const bool move = mloc > st.m + kLazyLog2;  // -inf > -inf is false: a fully masked column stays
+  if (__builtin_amdgcn_ballot_w64(move)) {
+    const float m_new = move ? mloc : st.m;
+    const float alpha = move ? fast_exp2(st.m - m_new) : 1.f;
+    st.l *= alpha;
+#pragma unroll
+    for (int mm = 0; mm < kMM; ++mm) st.acc[mm] *= alpha;
+    st.m = m_new;
+  }
+  const float mb = st.m == kNegInf ? 0.f : st.m;
   float pe[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(sv[e] - mb);
-  st.l = st.l * alpha + (((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7])));
-  st.m = m_new;
-#pragma unroll
-  for (int mm = 0; mm < kMM; ++mm) st.acc[mm] *= alpha;
+  st.l += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
 
   uint4 phi, plo;
   uint32_t* ph = reinterpret_cast<uint32_t*>(&phi);
@@ -401,23 +417,25 @@ __device__ __forceinline__ void attend_pair(const uint4 (&ka0)[N], const uint4 (
       pl[q2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p0 - (float)hh[0], p1 - (float)hh[1]));
     }
   }
+  static_assert(kMM == 2 * N, "16-bit types: two head-dim rows per V word");
 #pragma unroll
-  for (int mm = 0; mm < kMM; ++mm) {
-    const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
-    const int wd = mm >> 1;
-    uint4 a;
-    a.x = __builtin_amdgcn_perm(v0[1][wd], v0[0][wd], sel);
-    a.y = __builtin_amdgcn_perm(v0[3][wd], v0[2][wd], sel);
-    a.z = __builtin_amdgcn_perm(v1[1][wd], v1[0][wd], sel);
-    a.w = __builtin_amdgcn_perm(v1[3][wd], v1[2][wd], sel);
+  for (int wd = 0; wd < N; ++wd) {
+    const u32x4 ae = __builtin_shufflevector(va0[wd], va1[wd], 0, 1, 4, 5);  // row 2 wd
+    const u32x4 ao = __builtin_shufflevector(va0[wd], va1[wd], 2, 3, 6, 7);  // row 2 wd + 1
     if constexpr (DT == DT_BF16) {
-      const bf16x8 A = __builtin_bit_cast(bf16x8, a);
-      st.acc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, phi), st.acc[mm], 0, 0, 0);
-      st.acc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, plo), st.acc[mm], 0, 0, 0);
+      const bf16x8 hi = __builtin_bit_cast(bf16x8, phi), lo = __builtin_bit_cast(bf16x8, plo);
+      const bf16x8 Ae = __builtin_bit_cast(bf16x8, ae), Ao = __builtin_bit_cast(bf16x8, ao);
+      st.acc[2 * wd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ae, hi, st.acc[2 * wd], 0, 0, 0);
+      st.acc[2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ao, hi, st.acc[2 * wd + 1], 0, 0, 0);
+      st.acc[2 * wd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ae, lo, st.acc[2 * wd], 0, 0, 0);
+      st.acc[2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ao, lo, st.acc[2 * wd + 1], 0, 0, 0);
     } else {
-      const halfx8 A = __builtin_bit_cast(halfx8, a);
-      st.acc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(halfx8, phi), st.acc[mm], 0, 0, 0);
-      st.acc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(halfx8, plo), st.acc[mm], 0, 0, 0);
+      const halfx8 hi = __builtin_bit_cast(halfx8, phi), lo = __builtin_bit_cast(halfx8, plo);
+      const halfx8 Ae = __builtin_bit_cast(halfx8, ae), Ao = __builtin_bit_cast(halfx8, ao);
+      st.acc[2 * wd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ae, hi, st.acc[2 * wd], 0, 0, 0);
+      st.acc[2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, hi, st.acc[2 * wd + 1], 0, 0, 0);
+      st.acc[2 * wd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ae, lo, st.acc[2 * wd], 0, 0, 0);
+      st.acc[2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, lo, st.acc[2 * wd + 1], 0, 0, 0);
     }
   }
 }
@@ -1158,7 +1176,7 @@ __global__ __launch_bounds__(64) void attn_stream_merge_kernel(AttnParams prm) {
 // (the block table row read with scalar loads), parks it in LDS (K in the
 // A-operand staging order, V in its load order), and after a barrier every
 // wave runs QK, online softmax and PV over the stage's four sub-tiles for its
-// own 16 columns.  The next three stages' loads are in flight meanwhile.  A
+// own 16 columns.  The next stage's loads are in flight meanwhile.  A
 // workgroup that covers the whole context writes the output rows directly;
 // when a call has too few workgroups to fill the chip, each context is cut
 // into stage-aligned parts, one workgroup each, and a merge combines the
@@ -1291,35 +1309,42 @@ void attn_prefill_kernel(AttnParams prm) {
       *reinterpret_cast<uint4*>(&sK[b][w][tr * kRow + ((c ^ (tr & kSwz)) * 16)]) = t.k[kk];
     }
 #pragma unroll
-    for (int qd = 0; qd < N; ++qd)
-      *reinterpret_cast<uint4*>(&sV[b][w][(qd * 64 + lane) * 16]) =
-          make_uint4(t.v[0][qd], t.v[1][qd], t.v[2][qd], t.v[3][qd]);
+    for (int qd = 0; qd < N; ++qd) {
+      uint4 x;
+      if constexpr (DT == DT_F32) {
+        x = make_uint4(t.v[0][qd], t.v[1][qd], t.v[2][qd], t.v[3][qd]);
+      } else {  // the PV A-operand words of dim pair qd (attend_pair's va)
+        x.x = __builtin_amdgcn_perm(t.v[1][qd], t.v[0][qd], 0x05040100u);
+        x.y = __builtin_amdgcn_perm(t.v[3][qd], t.v[2][qd], 0x05040100u);
+        x.z = __builtin_amdgcn_perm(t.v[1][qd], t.v[0][qd], 0x07060302u);
+        x.w = __builtin_amdgcn_perm(t.v[3][qd], t.v[2][qd], 0x07060302u);
+      }
+      *reinterpret_cast<uint4*>(&sV[b][w][(qd * 64 + lane) * 16]) = x;
+    }
   };
 
   WaveState<kMM> st;
   st.reset();
   const float scale_log2 = prm.scale_log2;
   // QK, softmax and PV over the four sub-tiles of stage sg (LDS buffer b).
-  auto fetch = [&](uint4 (&ka)[N], uint32_t (&vv)[4][N], int b, int j) {
+  auto fetch_k = [&](uint4 (&ka)[N], int b, int j) {
     const int tr = lane & 15;
 #pragma unroll
     for (int kk = 0; kk < N; ++kk) {
       const int c = (lane >> 4) + 4 * kk;
       ka[kk] = *reinterpret_cast<const uint4*>(&sK[b][j][tr * kRow + ((c ^ (tr & kSwz)) * 16)]);
     }
+  };
+  auto fetch_v = [&](u32x4 (&va)[N], int b, int j) {
 #pragma unroll
-    for (int qd = 0; qd < N; ++qd) {
-      const uint4 x = *reinterpret_cast<const uint4*>(&sV[b][j][(qd * 64 + lane) * 16]);
-      vv[0][qd] = x.x;
-      vv[1][qd] = x.y;
-      vv[2][qd] = x.z;
-      vv[3][qd] = x.w;
-    }
+    for (int qd = 0; qd < N; ++qd) va[qd] = *reinterpret_cast<const u32x4*>(&sV[b][j][(qd * 64 + lane) * 16]);
   };
   auto valid_of = [&](int sub) {
     const int v = vis - sub * kSub;
     return v > kSub ? kSub : v;
   };
+  // tokens every real column of this wave sees (its group's first column)
+  const int vis_first = cg < ngrp ? n - L + (cg * kSub) / G + 1 : 0;
   // QK, softmax and PV over the four sub-tiles of stage sg (LDS buffer b):
   // two pairs for 16-bit types (a pair whose second sub-tile is past this
   // wave's limit masks it: every token there is past every column's limit),
@@ -1331,11 +1356,16 @@ void attn_prefill_kernel(AttnParams prm) {
         const int sub = sg * kWaves + j;
         if (sub < nsub_w) {
           uint4 ka0[N], ka1[N];
-          uint32_t v0[4][N], v1[4][N];
-          fetch(ka0, v0, b, j);
-          fetch(ka1, v1, b, j + 1);
-          attend_pair<DT, N, kMM>(ka0, ka1, v0, v1, qb, valid_of(sub), valid_of(sub + 1),
-                                  scale_log2, r, st);
+          u32x4 va0[N], va1[N];
+          fetch_k(ka0, b, j);
+          fetch_k(ka1, b, j + 1);
+          fetch_v(va0, b, j);
+          fetch_v(va1, b, j + 1);
+          if ((sub + 2) * kSub <= vis_first)
+            attend_pair<DT, N, kMM, false>(ka0, ka1, va0, va1, qb, kSub, kSub, scale_log2, r, st);
+          else
+            attend_pair<DT, N, kMM, true>(ka0, ka1, va0, va1, qb, valid_of(sub), valid_of(sub + 1),
+                                          scale_log2, r, st);
         }
       }
     } else {
@@ -1344,39 +1374,36 @@ void attn_prefill_kernel(AttnParams prm) {
         const int sub = sg * kWaves + j;
         if (sub < nsub_w) {
           uint4 ka[N];
+          u32x4 va[N];
           uint32_t vv[4][N];
-          fetch(ka, vv, b, j);
+          fetch_k(ka, b, j);
+          fetch_v(va, b, j);
+#pragma unroll
+          for (int qd = 0; qd < N; ++qd) {
+            vv[0][qd] = va[qd].x;
+            vv[1][qd] = va[qd].y;
+            vv[2][qd] = va[qd].z;
+            vv[3][qd] = va[qd].w;
+          }
           attend_core<DT, N, kMM>(ka, vv, qb, valid_of(sub), scale_log2, r, st);
         }
       }
     }
   };
-  // A ring of three register tiles keeps this wave's sub-tiles of the next
-  // three stages in flight: at stage sg the load of stage sg + 3 is issued,
-  // stage sg is computed from LDS, and stage sg + 1 is parked in the other
-  // buffer (whose last readers finished before the previous barrier).
-  Tile<N> t0, t1, t2;
-  load_sub(t0, st0 * kWaves + w);
-  load_sub(t1, (st0 + 1) * kWaves + w);
-  load_sub(t2, (st0 + 2) * kWaves + w);
-  park(t0, 0);
+  // One register tile keeps this wave's sub-tile of the next stage in flight
+  // while the current stage is computed from LDS; it is parked in the other
+  // buffer (whose last readers finished before the previous barrier).  (A
+  // ring of three tiles measured no faster: the core, not the loads, sets
+  // the pace.)
+  Tile<N> t;
+  load_sub(t, st0 * kWaves + w);
+  park(t, 0);
   __syncthreads();
-  // Rounds of three stages with no exit in between: every path issues the
-  // same loads, so each park waits for its own tile only.  Stages past the
-  // part load nothing and compute nothing.
-  for (int sg = st0; sg < st1; sg += 3) {
+  for (int sg = st0; sg < st1; ++sg) {
     const int b = (sg - st0) & 1;
-    load_sub(t0, (sg + 3) * kWaves + w);
+    load_sub(t, (sg + 1) * kWaves + w);
     compute_stage(sg, b);
-    park(t1, b ^ 1);
-    __syncthreads();
-    load_sub(t1, (sg + 4) * kWaves + w);
-    if (sg + 1 < st1) compute_stage(sg + 1, b ^ 1);
-    park(t2, b);
-    __syncthreads();
-    load_sub(t2, (sg + 5) * kWaves + w);
-    if (sg + 2 < st1) compute_stage(sg + 2, b);
-    park(t0, b ^ 1);
+    park(t, b ^ 1);
     __syncthreads();
   }
 
