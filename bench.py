@@ -15,7 +15,9 @@ launched by one paged_attention_decode call) against MI355X's 8 TB/s HBM
 peak, with its duration measured by HIP events on the launching stream;
 ``traffic`` is the HBM bytes the rocprofv3 counters measured for that call
 (profiles/, calibrated against a plain copy), reported only while the kernel
-source is the one the counters were taken on.  ``cpu_baseline`` times the CPU
+source is the one the counters were taken on.  A multi-token workload that
+takes the prefill path (prompt chunks) is priced instead on its attention
+flops against the dense MFMA peak of its dtype.  ``cpu_baseline`` times the CPU
 oracle on the same step's inputs.
 """
 
@@ -33,6 +35,9 @@ sys.path.insert(0, ROOT)
 from paged_kv_cache_388_amd import workloads as wl  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
+# dense MFMA peaks of MI355X, TFLOP/s, by the dtype the products run in
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+PREFILL_MIN_COLS = 64      # max_query_len * G at which a multi call takes the prefill path
 ATTN_SOURCE = os.path.join(ROOT, "paged_kv_cache_388_amd", "csrc", "attention.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) and seqs/s"
@@ -503,13 +508,21 @@ def main():
     for i in range(args.steps):
         if scrub is not None:
             scrub.fill_(i & 0xff)
-        wstarts[i].record(stream)
+            wstarts[i].record(stream)
         write_step()
         starts[i].record(stream)
         attend()
         ends[i].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if scrub is None:
+        # the cache writes alone, outside the timed region (an extra event per
+        # step inside it would lengthen the step it measures)
+        for i in range(args.steps):
+            wstarts[i].record(stream)
+            write_step()
+            starts[i].record(stream)
+        torch.cuda.synchronize()
     write_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(wstarts, starts)]))
 
     # the achievable-read reference on the same device: 4 GiB read once
@@ -543,6 +556,36 @@ def main():
         # the roofline is taken on the distinct bytes
         alg = alg - kv + uniq
     achieved = alg / (attn_avg_ms * 1e-3) / 1e9
+    flops = attention_flops(w)
+    G = w.num_q_heads // w.num_kv_heads
+    if w.multi and w.max_query_len * G >= PREFILL_MIN_COLS:
+        # the prefill path reads each context once per 64 columns and does
+        # 4*D flops per (column, visible token): far above the MFMA/HBM ridge
+        # (2.5 PFLOP/s / 8 TB/s = 312 flop/B), so it is priced on the matrix cores
+        tflops = flops / (attn_avg_ms * 1e-3) / 1e12
+        peak = PEAK_MFMA_TFLOPS[w.dtype]
+        roofline = {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None,
+                    "kernel": (f"attn_prefill_kernel<{w.dtype},{w.head_dim},{w.block_size}> "
+                               "(+ attn_prefill_merge_kernel when contexts are cut into "
+                               "parts; one paged_attention_multi call)"),
+                    "algorithmic_flops_per_launch": flops,
+                    "algorithmic_bytes_per_launch": alg,
+                    "hbm_GBps_of_algorithmic_bytes": round(achieved, 1)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                    "traffic": counter_traffic(w.name),
+                    "kernel": (f"attn_stream_kernel<{w.dtype},{w.head_dim},{w.block_size}> + "
+                               "attn_stream_merge_kernel (one "
+                               f"{'paged_attention_multi' if w.multi else 'paged_attention_decode'}"
+                               " call)"),
+                    "algorithmic_bytes_per_launch": alg,
+                    **({"kv_bytes_logical": kv, "kv_bytes_unique": uniq,
+                        "note": ("K/V shared between sequences: achieved counts each distinct "
+                                 "byte once; the distinct footprint fits in the Infinity "
+                                 "Cache, so a warm run is not HBM-bound (see --cold)")}
+                       if shared else {})}
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -568,7 +611,7 @@ def main():
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "seqs_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "new_tokens_per_s": round(w.q.shape[0] / (ms_per_step * 1e-3), 1),
-        "attention_tflops": round(attention_flops(w) / (attn_avg_ms * 1e-3) / 1e12, 2),
+        "attention_tflops": round(flops / (attn_avg_ms * 1e-3) / 1e12, 2),
         "cache_writes_ms": round(write_ms, 4),
         "read_probe_GBps": round(probe_gbs, 1),
         "frac_of_read_probe": round(achieved / probe_gbs, 4),
@@ -576,19 +619,7 @@ def main():
                          "p10": round(float(np.percentile(attn_ms, 10)), 4),
                          "p50": round(float(np.percentile(attn_ms, 50)), 4),
                          "p90": round(float(np.percentile(attn_ms, 90)), 4)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": counter_traffic(w.name),
-                     "kernel": (f"attn_stream_kernel<{w.dtype},{w.head_dim},{w.block_size}> + "
-                                "attn_stream_merge_kernel (one "
-                                f"{'paged_attention_multi' if w.multi else 'paged_attention_decode'}"
-                                " call)"),
-                     "algorithmic_bytes_per_launch": alg,
-                     **({"kv_bytes_logical": kv, "kv_bytes_unique": uniq,
-                         "note": ("K/V shared between sequences: achieved counts each distinct "
-                                  "byte once; the distinct footprint fits in the Infinity "
-                                  "Cache, so a warm run is not HBM-bound (see --cold)")}
-                        if shared else {})},
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
