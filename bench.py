@@ -501,6 +501,7 @@ def main():
     stream = torch.cuda.current_stream()
     scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold else None
     wstarts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    wends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -517,13 +518,16 @@ def main():
     t1 = time.perf_counter()
     if scrub is None:
         # the cache writes alone, outside the timed region (an extra event per
-        # step inside it would lengthen the step it measures)
+        # step inside it would lengthen the step it measures); they rewrite
+        # the same values into the same slots
         for i in range(args.steps):
             wstarts[i].record(stream)
             write_step()
-            starts[i].record(stream)
+            wends[i].record(stream)
         torch.cuda.synchronize()
-    write_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(wstarts, starts)]))
+    else:
+        wends = starts
+    write_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(wstarts, wends)]))
 
     # the achievable-read reference on the same device: 4 GiB read once
     probe_src = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
