@@ -1010,6 +1010,27 @@ void attn_stream_kernel(AttnParams prm) {
   int vis_c = 0;  // this lane's column: tokens it can see (0 for a padding column)
   uint4 qb[N];
   WaveState<kMM> st;
+  // Slot 0's state, when its piece ends before the chunk does, stays in
+  // registers until the chunk's end.  Stores share the vector memory counter
+  // with loads and it retires in order, so a store issued mid-stream makes
+  // every tile load issued after it wait for the store's acknowledgement.
+  // (Not for fp32 at D = 128, whose wider tiles leave no registers for it.)
+  constexpr bool kHold = !(DT == DT_F32 && D > 64);
+  float held_o[D / 4];
+  float held_m = 0.f, held_l = 0.f;
+  float* held_dst = nullptr;
+  bool held = false;
+  auto store_slot = [&](float* dst, const float (&o)[D / 4], float m, float l) {
+    if ((lane & 15) < cols) {
+      store_run<DT_F32, D>(dst + r * (D / 4), o);
+      if (r == 0) *reinterpret_cast<float2*>(prm.part_ml + (dst - prm.part_o) / D * 2) =
+          make_float2(m, l);
+    }
+  };
+  auto store_held = [&]() {
+    if (held) store_slot(held_dst, held_o, held_m, held_l);
+    held = false;
+  };
   auto finish_piece = [&](int p_end) {
     float l = st.l + __shfl_xor(st.l, 16);
     l += __shfl_xor(l, 32);
@@ -1026,11 +1047,21 @@ void attn_stream_kernel(AttnParams prm) {
         for (int i = 0; i < D / 4; ++i) o[i] *= inv;
         store_run<DT, D>(static_cast<char*>(prm.out) + (row * D + r * (D / 4)) * Geo::EB, o);
       }
-    } else if (col < cols) {
+    } else {
+      // slot rows of columns >= cols lie past the slot: never stored
       const size_t slot = (size_t)wv * 2 + (p0 == a ? 0 : 1);
-      store_run<DT_F32, D>(prm.part_o + (slot * cols + col) * D + r * (D / 4), o);
-      if (r == 0)
-        *reinterpret_cast<float2*>(prm.part_ml + (slot * cols + col) * 2) = make_float2(st.m, l);
+      float* dst = prm.part_o + (slot * cols + (col < cols ? col : 0)) * D;
+      if (!kHold || p_end == b) {
+        store_held();
+        store_slot(dst, o, st.m, l);
+      } else {  // only slot 0 ends before the chunk does
+#pragma unroll
+        for (int i = 0; i < D / 4; ++i) held_o[i] = o[i];
+        held_m = st.m;
+        held_l = l;
+        held_dst = dst;
+        held = true;
+      }
     }
   };
   auto step = [&](Tile<N>& t, const SlotMeta& m) {
@@ -1084,6 +1115,7 @@ void attn_stream_kernel(AttnParams prm) {
     if (m2.p < 0) break;
     step(t2, m2);
   }
+  store_held();  // the chunk ended in a whole group
 }
 
 // Merge of the pieces of one split (sequence, kv head, column group) for one
