@@ -860,6 +860,18 @@ __device__ __forceinline__ int group_rows(const SeqCols& sc, int cg, int G, int 
   return v > kSub ? kSub : v;
 }
 
+template <int D>
+__device__ __forceinline__ void load_run(const float* src, float (&o)[D / 4]) {
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    const float4 x = reinterpret_cast<const float4*>(src)[i];
+    o[4 * i] = x.x;
+    o[4 * i + 1] = x.y;
+    o[4 * i + 2] = x.z;
+    o[4 * i + 3] = x.w;
+  }
+}
+
 template <int DT, int D, int BS, bool MULTI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_stream_kernel(AttnParams prm) {
@@ -867,12 +879,29 @@ void attn_stream_kernel(AttnParams prm) {
   constexpr int N = Geo::N;
   constexpr int kMM = Geo::kMM;
   constexpr int kMaxSeqs = MULTI ? kMaxMultiSeqs : kMaxStreamSeqs;
-  __shared__ int sS[kMaxSeqs + 1];
-  __shared__ int sCtx[kMaxSeqs];
-  __shared__ int sQS[MULTI ? kMaxSeqs : 1];  // first query row
-  __shared__ int sQL[MULTI ? kMaxSeqs : 1];  // query rows
+  // Per-sequence tables: sS [B + 1] position prefix, sCtx [B] context
+  // lengths, and with several new tokens sQS [B] first query row, sQL [B]
+  // query rows.  Once every wave has left its loop the same memory carries
+  // the waves' first-piece states (sX).
+  constexpr int kTabInts = 2 * kMaxSeqs + 1 + (MULTI ? 2 * kMaxSeqs : 0);
+  __shared__ __attribute__((aligned(16))) int sTab[kTabInts];
+  static_assert(kWaves * 64 * (D / 4) * sizeof(float) <= kTabInts * sizeof(int),
+                "first-piece states fit the tables");
+  int* const sS = sTab;
+  int* const sCtx = sTab + kMaxSeqs + 1;
+  int* const sQS = sCtx + kMaxSeqs;
+  int* const sQL = sQS + (MULTI ? kMaxSeqs : 0);
   __shared__ int sScan[kWaves];
   __shared__ __attribute__((aligned(16))) char sK[kWaves][kSub * Geo::kRow];
+  // The chunk's last piece, when partial, is parked in LDS as it finishes:
+  // 16-byte chunks i < kInK of each lane's run in the wave's K staging slot
+  // (no longer needed then), the rest in sX1.
+  constexpr int kRunChunks = D / 16;
+  constexpr int kInK = (int)(sizeof(sK[0]) / (64 * 16)) < kRunChunks ? (int)(sizeof(sK[0]) / (64 * 16))
+                                                                      : kRunChunks;
+  __shared__ __attribute__((aligned(16))) float4 sX1[kWaves][(kRunChunks - kInK) * 64 + 1];
+  __shared__ float2 sML[2][kWaves][kSub];  // (max, normaliser) per column: first, last piece
+  __shared__ int sInfo[2][kWaves][6];      // span of the first / last piece: A, E, h, cg, q0, L
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -938,10 +967,14 @@ void attn_stream_kernel(AttnParams prm) {
   const int per = uniform(sS[B]);  // positions per kv head
   const int total = prm.num_kv_heads * per;
   const int chunk = stream_chunk(total, (int)gridDim.x * kWaves);
-  const int wv = xcd_remap(blockIdx.x, gridDim.x) * kWaves + w;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int wv = wg * kWaves + w;
+  // end of wave v's chunk (v = kWaves * wg + i); the workgroup's positions
+  // are [ga, end of wave kWaves * wg + kWaves - 1)
+  auto chunk_end = [&](int v) -> int { return (int)min((long long)(v + 1) * chunk, (long long)total); };
   const int a = (int)min((long long)wv * chunk, (long long)total);
-  const int b = a + chunk < total ? a + chunk : total;
-  if (a >= b) return;  // no block-wide barrier follows
+  const int b = chunk_end(wv);
+  const int ga = (int)min((long long)wg * kWaves * chunk, (long long)total);
 
   const int koff = 16 * lane;
   const int voff = (4 * r) * Geo::kRow + (lane & 15) * (4 * N);
@@ -999,10 +1032,18 @@ void attn_stream_kernel(AttnParams prm) {
   };
 
   // ---- compute cursor -----------------------------------------------------------
-  // The open piece: positions [p0, ...) of group span sc.  A piece that does
-  // not cover its whole group sits in partial slot 0 of this wave if it
-  // starts the chunk, else in slot 1 (only the chunk's last piece can).
+  // The open piece: positions [p0, ...) of group span sc.  A piece that covers
+  // its whole group is written to `out` at once.  Otherwise it is the chunk's
+  // first piece or its last one (ending at b), and nothing of it goes to
+  // global memory inside the loop: stores share the vector memory counter
+  // with loads and it retires in order, so a store issued mid-stream makes
+  // every tile load issued after it wait for the store's acknowledgement.
+  // The first piece's run stays in registers (fp32 at D = 128, whose wider
+  // tiles leave no room, parks it in this wave's workspace row instead); the
+  // last piece's run goes to LDS.  The spans' identities go to sInfo.
+  constexpr bool kHold = !(DT == DT_F32 && D > 64);
   const int cols = prm.slot_cols;
+  const int col = lane & 15;
   bool open = false;
   int p0 = 0;
   SeqSpan sc;
@@ -1010,58 +1051,59 @@ void attn_stream_kernel(AttnParams prm) {
   int vis_c = 0;  // this lane's column: tokens it can see (0 for a padding column)
   uint4 qb[N];
   WaveState<kMM> st;
-  // Slot 0's state, when its piece ends before the chunk does, stays in
-  // registers until the chunk's end.  Stores share the vector memory counter
-  // with loads and it retires in order, so a store issued mid-stream makes
-  // every tile load issued after it wait for the store's acknowledgement.
-  // (Not for fp32 at D = 128, whose wider tiles leave no registers for it.)
-  constexpr bool kHold = !(DT == DT_F32 && D > 64);
-  float held_o[D / 4];
-  float held_m = 0.f, held_l = 0.f;
-  float* held_dst = nullptr;
-  bool held = false;
-  auto store_slot = [&](float* dst, const float (&o)[D / 4], float m, float l) {
-    if ((lane & 15) < cols) {
-      store_run<DT_F32, D>(dst + r * (D / 4), o);
-      if (r == 0) *reinterpret_cast<float2*>(prm.part_ml + (dst - prm.part_o) / D * 2) =
-          make_float2(m, l);
+  float o0[D / 4];  // the first piece's run
+  float m0 = 0.f, l0 = 0.f;
+  bool has0 = false, has1 = false;
+  float* const park = prm.part_o + (((size_t)gridDim.x * 2 + wv) * cols + (col < cols ? col : 0)) * D +
+                      r * (D / 4);
+  auto x1_chunk = [&](int i) -> float4& {
+    return i < kInK ? reinterpret_cast<float4*>(sK[w])[i * 64 + lane] : sX1[w][(i - kInK) * 64 + lane];
+  };
+  // normalise a group's finished state and write its rows
+  auto write_out = [&](float (&o)[D / 4], float l, int h, int cg, int q0, int L, int col, int r) {
+    const int c = cg * kSub + col;
+    if (c < L * G) {
+      const size_t row = MULTI ? (size_t)(q0 + c / G) * Hq + (size_t)h * G + c % G
+                               : (size_t)q0 * Hq + (size_t)h * G + c;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i) o[i] *= inv;
+      store_run<DT, D>(static_cast<char*>(prm.out) + (row * D + r * (D / 4)) * Geo::EB, o);
     }
   };
-  auto store_held = [&]() {
-    if (held) store_slot(held_dst, held_o, held_m, held_l);
-    held = false;
+  auto note_span = [&](int k) {
+    if (lane == 0) {
+      sInfo[k][w][0] = sc.A;
+      sInfo[k][w][1] = sc.E;
+      sInfo[k][w][2] = sc.h;
+      sInfo[k][w][3] = sc.cg;
+      sInfo[k][w][4] = cc.q0;
+      sInfo[k][w][5] = cc.L;
+    }
   };
   auto finish_piece = [&](int p_end) {
     float l = st.l + __shfl_xor(st.l, 16);
     l += __shfl_xor(l, 32);
-    const int col = lane & 15;
-    const int c = sc.cg * kSub + col;
     float o[D / 4];
     lane_run<D, kMM>(o, st);
     if (p0 == sc.A && p_end == sc.E) {
-      if (c < cc.L * G) {
-        const size_t row = MULTI ? (size_t)(cc.q0 + c / G) * Hq + (size_t)sc.h * G + c % G
-                                 : (size_t)cc.q0 * Hq + (size_t)sc.h * G + c;
-        const float inv = l > 0.f ? 1.f / l : 0.f;
+      write_out(o, l, sc.h, sc.cg, cc.q0, cc.L, col, r);
+    } else if (p0 == a) {
 #pragma unroll
-        for (int i = 0; i < D / 4; ++i) o[i] *= inv;
-        store_run<DT, D>(static_cast<char*>(prm.out) + (row * D + r * (D / 4)) * Geo::EB, o);
-      }
-    } else {
-      // slot rows of columns >= cols lie past the slot: never stored
-      const size_t slot = (size_t)wv * 2 + (p0 == a ? 0 : 1);
-      float* dst = prm.part_o + (slot * cols + (col < cols ? col : 0)) * D;
-      if (!kHold || p_end == b) {
-        store_held();
-        store_slot(dst, o, st.m, l);
-      } else {  // only slot 0 ends before the chunk does
+      for (int i = 0; i < D / 4; ++i) o0[i] = o[i];
+      m0 = st.m;
+      l0 = l;
+      has0 = true;
+      note_span(0);
+      if constexpr (!kHold)
+        if (col < cols) store_run<DT_F32, D>(park, o0);
+    } else {  // only the chunk's last piece can be partial without starting it
 #pragma unroll
-        for (int i = 0; i < D / 4; ++i) held_o[i] = o[i];
-        held_m = st.m;
-        held_l = l;
-        held_dst = dst;
-        held = true;
-      }
+      for (int i = 0; i < D / 16; ++i)
+        x1_chunk(i) = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+      if (r == 0) sML[1][w][col] = make_float2(st.m, l);
+      has1 = true;
+      note_span(1);
     }
   };
   auto step = [&](Tile<N>& t, const SlotMeta& m) {
@@ -1099,23 +1141,111 @@ void attn_stream_kernel(AttnParams prm) {
     }
   };
 
-  enter_issue_seq();
-  Tile<N> t0, t1, t2;
-  SlotMeta m0, m1, m2;
-  issue(t0, m0);
-  issue(t1, m1);
-  for (;;) {
-    issue(t2, m2);
-    if (m0.p < 0) break;
-    step(t0, m0);
+  if (a < b) {
+    enter_issue_seq();
+    Tile<N> t0, t1, t2;
+    SlotMeta m0, m1, m2;
     issue(t0, m0);
-    if (m1.p < 0) break;
-    step(t1, m1);
     issue(t1, m1);
-    if (m2.p < 0) break;
-    step(t2, m2);
+    for (;;) {
+      issue(t2, m2);
+      if (m0.p < 0) break;
+      step(t0, m0);
+      issue(t0, m0);
+      if (m1.p < 0) break;
+      step(t1, m1);
+      issue(t1, m1);
+      if (m2.p < 0) break;
+      step(t2, m2);
+    }
   }
-  store_held();  // the chunk ended in a whole group
+
+  // ---- the workgroup's pieces ---------------------------------------------------
+  // The four waves hold consecutive chunks.  A group span that crosses a
+  // chunk boundary inside the workgroup is merged here, in logical order, by
+  // the wave that holds its first piece in the workgroup: a span that starts
+  // and ends inside the workgroup is written to `out`; otherwise the merged
+  // piece goes to the workgroup's slot 0 (the span starts at or before the
+  // workgroup's first position) or slot 1, and the merge kernel finishes it.
+  __syncthreads();  // every wave has left its loop: the tables are free
+  // The lane index again, opaque to the compiler: addresses derived from it
+  // below are not hoisted above the loop, where they would stay live in
+  // registers the loop needs.
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int lcol = ln & 15, lr = ln >> 4;
+  float4* const sX0 = reinterpret_cast<float4*>(sTab);  // first pieces: [kWaves][D/16][64 lanes]
+  if (has0) {
+    if constexpr (!kHold)
+      if (lcol < cols) load_run<D>(park, o0);
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i)
+      sX0[(w * (D / 16) + i) * 64 + ln] = make_float4(o0[4 * i], o0[4 * i + 1], o0[4 * i + 2],
+                                                        o0[4 * i + 3]);
+    if (lr == 0) sML[0][w][lcol] = make_float2(m0, l0);
+  }
+  __syncthreads();
+  // o, m, l: the state of a piece ending at this wave's chunk end (k: which
+  // piece, for its span); merges the next waves' first pieces while the span
+  // goes on, then writes the result
+  auto finish_span = [&](float (&o)[D / 4], float m, float l, int k) {
+    const int A = uniform(sInfo[k][w][0]), E = uniform(sInfo[k][w][1]);
+    int v = w;
+    int bv = b;
+    while (E > bv && v + 1 < kWaves) {  // the next wave's first piece continues it
+      ++v;
+      bv = chunk_end(wg * kWaves + v);
+      const float2 ml = sML[0][v][lcol];
+      const float M = fmaxf(m, ml.x);
+      const float fa = m == kNegInf ? 0.f : fast_exp2(m - M);
+      const float fb = ml.x == kNegInf ? 0.f : fast_exp2(ml.x - M);
+      l = fa * l + fb * ml.y;
+      m = M;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        const float4 x = sX0[(v * (D / 16) + i) * 64 + ln];
+        o[4 * i] = fa * o[4 * i] + fb * x.x;
+        o[4 * i + 1] = fa * o[4 * i + 1] + fb * x.y;
+        o[4 * i + 2] = fa * o[4 * i + 2] + fb * x.z;
+        o[4 * i + 3] = fa * o[4 * i + 3] + fb * x.w;
+      }
+    }
+    if (A >= ga && E <= bv) {
+      write_out(o, l, uniform(sInfo[k][w][2]), uniform(sInfo[k][w][3]), uniform(sInfo[k][w][4]),
+                uniform(sInfo[k][w][5]), lcol, lr);
+    } else if (lcol < cols) {  // slot rows of columns >= cols lie past the slot
+      const size_t slot = (size_t)wg * 2 + (A <= ga ? 0 : 1);
+      store_run<DT_F32, D>(prm.part_o + (slot * cols + lcol) * D + lr * (D / 4), o);
+      if (lr == 0) *reinterpret_cast<float2*>(prm.part_ml + (slot * cols + lcol) * 2) = make_float2(m, l);
+    }
+  };
+  // a first piece that started before this chunk belongs to the previous
+  // wave's span, unless this wave starts the workgroup
+  // (each state is read back from LDS: taking the first piece's registers
+  // here instead would make the loop above spill)
+  auto own_state = [&](int k, float (&o)[D / 4]) -> float2 {
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      const float4 x = k == 0 ? sX0[(w * (D / 16) + i) * 64 + ln]
+                     : i < kInK ? reinterpret_cast<const float4*>(sK[w])[i * 64 + ln]
+                                : sX1[w][(i - kInK) * 64 + ln];
+      o[4 * i] = x.x;
+      o[4 * i + 1] = x.y;
+      o[4 * i + 2] = x.z;
+      o[4 * i + 3] = x.w;
+    }
+    return sML[k][w][lcol];
+  };
+  if (has0 && (w == 0 || uniform(sInfo[0][w][0]) >= a)) {
+    float o[D / 4];
+    const float2 ml = own_state(0, o);
+    finish_span(o, ml.x, ml.y, 0);
+  }
+  if (has1) {
+    float o[D / 4];
+    const float2 ml = own_state(1, o);
+    finish_span(o, ml.x, ml.y, 1);
+  }
 }
 
 // Merge of the pieces of one split (sequence, kv head, column group) for one
@@ -1159,13 +1289,15 @@ __global__ __launch_bounds__(64) void attn_stream_merge_kernel(AttnParams prm) {
   if (c >= L * G) return;
   const size_t orow = ((size_t)(q0 + c / G) * Hq + (size_t)h * G + c % G) * D;
   const int per = prm.seq_prefix[prm.num_seqs];
-  const int chunk = stream_chunk(prm.num_kv_heads * per, prm.stream_wgs * kWaves);
+  // a workgroup's positions: kWaves consecutive wave chunks
+  const int chunk = kWaves * stream_chunk(prm.num_kv_heads * per, prm.stream_wgs * kWaves);
   const int nsub = (ctx + kSub - 1) / kSub;
   const int A = h * per + prm.seq_prefix[s] + cg * nsub;
   const int E = A + nsub;
   const int k1 = A / chunk, k2 = (E - 1) / chunk;
-  if (k1 == k2) return;  // one wave covered it and wrote `out`
-  // wave k's piece sits in its slot 0 unless the group starts inside chunk k1
+  if (k1 == k2) return;  // one workgroup covered it and wrote `out`
+  // workgroup k's piece sits in its slot 0 unless the group starts inside
+  // the positions of workgroup k1
   const int first_slot = k1 * 2 + (A != k1 * chunk ? 1 : 0);
   auto row_of = [&](int k) -> size_t { return (size_t)(k == k1 ? first_slot : k * 2) * cols + col; };
 
@@ -1603,7 +1735,8 @@ AttnWorkspace attn_workspace_layout(int32_t num_seqs, int32_t slot_cols, int32_t
   AttnWorkspace ws{0, 0, 0, 0};
   if (num_seqs <= 0 || num_q_heads <= 0 || slot_cols <= 0 || head_dim <= 0) return ws;
   if (stream_wgs > 0) {
-    const size_t slots = (size_t)stream_wgs * kWaves * 2;
+    // two piece slots per workgroup, then one parking row per wave
+    const size_t slots = (size_t)stream_wgs * (2 + kWaves);
     ws.prefix_off = 0;
     ws.part_o_off = align256(sizeof(int32_t) * ((size_t)num_seqs + 1));
     ws.part_ml_off = align256(ws.part_o_off + slots * slot_cols * head_dim * sizeof(float));

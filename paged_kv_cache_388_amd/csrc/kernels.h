@@ -15,9 +15,11 @@ constexpr int kSubTokens = 16;
 // ---- stream path (default) -------------------------------------------------
 // Workgroups of 4 independent waves, two per compute unit.  The work of one
 // call is the ordered list of (kv head, sequence, 16-token sub-tile)
-// positions; wave v of the grid takes positions [v * chunk, (v + 1) * chunk).
-// A wave finishes each sequence piece it covers: a whole sequence is written
-// straight to `out`, a piece of one to one of the wave's two partial slots,
+// positions; wave v of the grid takes positions [v * chunk, (v + 1) * chunk),
+// so a workgroup holds 4 consecutive chunks.  A wave writes a whole sequence
+// it covers straight to `out`; the pieces of a sequence cut by chunk
+// boundaries are merged inside the workgroup at its end, and what crosses a
+// workgroup boundary goes to one of the workgroup's two partial slots,
 // merged afterwards in logical order.
 constexpr int kStreamWaves = 4;           // waves per workgroup
 constexpr int kMaxStreamSeqs = 4096;      // batch limit (per-sequence tables live in LDS)
@@ -60,8 +62,9 @@ struct AttnParams {
   int32_t max_context_len;
   float scale_log2;             // scale * log2(e): logits kept in base-2 units
   // Workspace views.  Stream path: seq_prefix [B + 1] (sub-tiles of the
-  // sequences before each one), part_o [2 * waves, G, D], part_ml
-  // [2 * waves, G, 2] (max logit in log2 units, normaliser).  Grid path:
+  // sequences before each one), part_o [2 * workgroups + waves, slot_cols, D]
+  // (two partial slots per workgroup, then a parking row per wave), part_ml
+  // [same rows, slot_cols, 2] (max logit in log2 units, normaliser).  Grid path:
   // part_o [B, H_q, P, D], part_ml [B, H_q, P, 2]; seq_prefix unused.
   int32_t* seq_prefix;
   float* part_o;
