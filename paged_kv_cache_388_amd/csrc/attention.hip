@@ -1324,6 +1324,89 @@ __global__ __launch_bounds__(64) void attn_stream_merge_kernel(AttnParams prm) {
   for (int j = 0; j < kPer; ++j) store_out<DT>(prm.out, orow + lane + 64 * j, o[j] * inv);
 }
 
+// The same merge for calls whose partial slots hold 16 columns (several new
+// tokens per sequence): one wave per (sequence, kv head, column group), lane
+// (r, col) holding column col's run d in [r*D/4, (r+1)*D/4) exactly as the
+// stream kernel stores it; the workgroups' pieces are folded in logical order
+// with a running max.  (With fewer columns most lanes would idle and a
+// group's pieces would be fetched one after another: the per-column kernel
+// is faster there.)  Grid: sequence x kv head x group (up to the call's
+// maximum).
+template <int DT, int D, bool MULTI>
+__global__ __launch_bounds__(64) void attn_stream_merge_group_kernel(AttnParams prm) {
+  using Geo = Geometry<DT, D, 16>;
+  const int lane = threadIdx.x;
+  const int r = lane >> 4, col = lane & 15;
+  const int Hq = prm.num_q_heads;
+  const int G = prm.group;
+  const int cols = prm.slot_cols;
+  const int ngmax = prm.max_groups;
+  int id = blockIdx.x;
+  const int cg = id % ngmax;
+  id /= ngmax;
+  const int h = id % prm.num_kv_heads;
+  const int s = id / prm.num_kv_heads;
+  int ctx = prm.context_lens[s];
+  ctx = ctx < 0 ? 0 : (ctx > prm.max_context_len ? prm.max_context_len : ctx);
+  int q0 = s, L = ctx > 0 ? 1 : 0;
+  if constexpr (MULTI) {
+    const int T = prm.num_query_tokens;
+    q0 = prm.query_start[s];
+    int qe = prm.query_start[s + 1];
+    q0 = q0 < 0 ? 0 : (q0 > T ? T : q0);
+    qe = qe < q0 ? q0 : (qe > T ? T : qe);
+    L = qe - q0;
+    L = L < ctx ? L : ctx;
+    L = L < prm.max_query_len ? L : prm.max_query_len;
+  } else if (ctx == 0) {
+    if (col < G) {
+      float z[D / 4];
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i) z[i] = 0.f;
+      store_run<DT, D>(static_cast<char*>(prm.out) +
+                           ((((size_t)s * Hq + (size_t)h * G + col) * D) + r * (D / 4)) * Geo::EB,
+                       z);
+    }
+    return;
+  }
+  const int c = cg * kSub + col;
+  if (c >= L * G || col >= cols) return;  // no cross-lane step follows
+  const int per = prm.seq_prefix[prm.num_seqs];
+  // a workgroup's positions: kWaves consecutive wave chunks
+  const int chunk = kWaves * stream_chunk(prm.num_kv_heads * per, prm.stream_wgs * kWaves);
+  const int nsub = (ctx + kSub - 1) / kSub;
+  const int A = h * per + prm.seq_prefix[s] + cg * nsub;
+  const int E = A + nsub;
+  const int k1 = A / chunk, k2 = (E - 1) / chunk;
+  if (k1 == k2) return;  // one workgroup covered it and wrote `out`
+  // workgroup k's piece sits in its slot 0 unless the group starts inside
+  // the positions of workgroup k1
+  const int first_slot = k1 * 2 + (A != k1 * chunk ? 1 : 0);
+  float M = kNegInf, lsum = 0.f;
+  float o[D / 4];
+#pragma unroll
+  for (int i = 0; i < D / 4; ++i) o[i] = 0.f;
+#pragma unroll 2
+  for (int k = k1; k <= k2; ++k) {
+    const size_t row = (size_t)(k == k1 ? first_slot : k * 2) * cols + col;
+    const float2 ml = *reinterpret_cast<const float2*>(prm.part_ml + row * 2);
+    float x[D / 4];
+    load_run<D>(prm.part_o + row * D + r * (D / 4), x);
+    const float Mn = fmaxf(M, ml.x);
+    const float fa = M == kNegInf ? 0.f : fast_exp2(M - Mn);
+    const float fb = ml.x == kNegInf ? 0.f : fast_exp2(ml.x - Mn);
+    lsum = fa * lsum + fb * ml.y;
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) o[i] = fa * o[i] + fb * x[i];
+    M = Mn;
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 4; ++i) o[i] *= inv;
+  const size_t orow = (size_t)(q0 + c / G) * Hq + (size_t)h * G + c % G;
+  store_run<DT, D>(static_cast<char*>(prm.out) + (orow * D + r * (D / 4)) * Geo::EB, o);
+}
+
 // ===========================================================================
 // Launch
 // ===========================================================================
@@ -1677,16 +1760,20 @@ hipError_t launch_typed(const AttnParams& prm, hipStream_t stream) {
     return hipGetLastError();
   }
   if (prm.stream_wgs > 0) {
-    const long long nmerge =
-        (long long)prm.num_seqs * prm.num_kv_heads * prm.max_groups * prm.slot_cols;
+    const long long ngroups = (long long)prm.num_seqs * prm.num_kv_heads * prm.max_groups;
+    const long long nmerge = ngroups * prm.slot_cols;
     if (nmerge > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (prm.query_start) {
       hipLaunchKernelGGL((attn_stream_kernel<DT, D, BS, true>), dim3((unsigned)prm.stream_wgs),
                          block, 0, stream, prm);
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
-      hipLaunchKernelGGL((attn_stream_merge_kernel<DT, D, true>), dim3((unsigned)nmerge), dim3(64),
-                         0, stream, prm);
+      if (prm.slot_cols == kSub)
+        hipLaunchKernelGGL((attn_stream_merge_group_kernel<DT, D, true>), dim3((unsigned)ngroups),
+                           dim3(64), 0, stream, prm);
+      else
+        hipLaunchKernelGGL((attn_stream_merge_kernel<DT, D, true>), dim3((unsigned)nmerge), dim3(64),
+                           0, stream, prm);
       return hipGetLastError();
     }
     hipLaunchKernelGGL((attn_stream_kernel<DT, D, BS, false>), dim3((unsigned)prm.stream_wgs),
