@@ -32,7 +32,11 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from paged_kv_cache_388_amd import workloads as wl  # noqa: E402
+# Worker processes of the CPU baseline re-import this file; they need only
+# NumPy and the oracle, not the library (or torch).
+_CPU_WORKER = os.environ.get("PKV_BENCH_CPU_WORKER") == "1"
+if not _CPU_WORKER:
+    from paged_kv_cache_388_amd import workloads as wl  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 # dense MFMA peaks of MI355X, TFLOP/s, by the dtype the products run in
@@ -102,15 +106,80 @@ def counter_traffic(workload):
     return int(fields["traffic_bytes_per_call"])
 
 
-def cpu_baseline(w, min_seconds):
-    """The fp64 oracle on this step's inputs, single-threaded (BLAS pinned to
-    one thread): the step's cache writes into the host pools, then attention
-    over every sequence, repeated until about ``min_seconds`` have passed.
-    Rate in KV GB/s (and sequences/s) of the attention passes it finished."""
+def _oracle_pass(A, seq_list, seconds):
+    """The oracle over the sequences of seq_list, round after round, until
+    ``seconds`` have passed: (query rows, sequence-attentions, KV bytes).  A
+    holds the step's host arrays (pools after the cache writes) and shape
+    facts.  A multi-token sequence's new rows go in slices of up to 16: a
+    slice of rows [a, e) is the last e - a tokens of a context of n - L + e
+    tokens, which is what each of its rows sees."""
+    import oracle
+    rows = seqs = kv = 0
+    per_token = 2 * A["num_kv_heads"] * A["head_dim"] * A["elem_bytes"]
+    t1 = time.perf_counter()
+    while True:
+        for s in seq_list:
+            if A["multi"]:
+                r0, r1 = int(A["query_start"][s]), int(A["query_start"][s + 1])
+                n, L = int(A["context_lens"][s]), r1 - r0
+                for a in range(0, L, 16):
+                    e = min(a + 16, L)
+                    oracle.multi_query_attention(
+                        A["q"][r0 + a:r0 + e], A["k_cache"], A["v_cache"], A["block_tables"][s:s + 1],
+                        np.array([n - L + e], dtype=np.int32), [e - a], A["scale"], A["dtype"])
+                    kv += (n - L + e) * per_token
+                    rows += e - a
+                    if time.perf_counter() - t1 > seconds:
+                        break
+            else:
+                oracle.decode_attention(A["q"], A["k_cache"], A["v_cache"], A["block_tables"],
+                                        A["context_lens"], A["scale"], A["dtype"], seq_ids=[s])
+                kv += int(A["context_lens"][s]) * per_token
+                rows += 1
+            seqs += 1
+            if time.perf_counter() - t1 > seconds:
+                return rows, seqs, kv
+        if not seq_list:
+            return rows, seqs, kv
+
+
+_WORKER_ARRAYS = {}
+
+
+def _oracle_worker_init(arrays, facts):
+    """A spawned baseline worker: one BLAS thread, the step's arrays mapped
+    from shared memory."""
+    from multiprocessing import shared_memory
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+    for name, (shm_name, shape, dtype) in arrays.items():
+        shm = shared_memory.SharedMemory(name=shm_name)
+        _WORKER_ARRAYS["_shm_" + name] = shm
+        _WORKER_ARRAYS[name] = np.ndarray(shape, dtype=np.dtype(dtype), buffer=shm.buf)
+    _WORKER_ARRAYS.update(facts)
+
+
+def _oracle_worker_run(task):
+    idx, workers, seconds = task
+    A = _WORKER_ARRAYS
+    return _oracle_pass(A, list(range(idx, A["num_seqs"], workers)), seconds)
+
+
+def cpu_baseline(w, min_seconds, workers):
+    """The fp64 oracle on this step's inputs: the step's cache writes into the
+    host pools (one thread), then attention over the batch's sequences split
+    round-robin over ``workers`` spawned processes of one BLAS thread each
+    (the pools shared through shared memory), each repeating its sequences
+    for about ``min_seconds``.  Also a one-process pass of a third of that
+    time, for the scaling.  Rates in KV GB/s (and query rows/s) of the
+    attention work finished."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    from concurrent.futures.process import BrokenProcessPool
+    from multiprocessing import shared_memory
     from threadpoolctl import threadpool_limits
 
     import oracle
-    b = wl.ELEM_BYTES[w.dtype]
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         kc, vc = w.k_cache, w.v_cache
@@ -118,44 +187,70 @@ def cpu_baseline(w, min_seconds):
             kc, vc = oracle.copy_blocks(kc, vc, w.block_mapping)
         if len(w.slot_mapping):
             kc, vc = oracle.kv_append(kc, vc, w.new_key, w.new_value, w.slot_mapping)
+        t_writes = time.perf_counter() - t0
+        arrays = {"k_cache": kc, "v_cache": vc, "q": w.q, "block_tables": w.block_tables,
+                  "context_lens": w.context_lens}
+        if w.multi:
+            arrays["query_start"] = w.query_start
+        facts = {"num_seqs": w.num_seqs, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                 "elem_bytes": wl.ELEM_BYTES[w.dtype], "multi": bool(w.multi), "scale": w.scale,
+                 "dtype": w.dtype}
+        one_s = min_seconds / 3
         t1 = time.perf_counter()
-        seqs = 0
-        rows = 0
-        kv = 0
-        while True:
-            for s in range(w.num_seqs):
-                if w.multi:
-                    # the sequence's new rows in slices of up to 16: a slice of
-                    # rows [a, e) is the last e - a tokens of a context of
-                    # n - L + e tokens, which is what each of its rows sees
-                    r0, r1 = int(w.query_start[s]), int(w.query_start[s + 1])
-                    n, L = int(w.context_lens[s]), r1 - r0
-                    for a in range(0, L, 16):
-                        e = min(a + 16, L)
-                        oracle.multi_query_attention(
-                            w.q[r0 + a:r0 + e], kc, vc, w.block_tables[s:s + 1],
-                            np.array([n - L + e], dtype=np.int32), [e - a], w.scale, w.dtype)
-                        kv += 2 * (n - L + e) * w.num_kv_heads * w.head_dim * b
-                        rows += e - a
-                        if time.perf_counter() - t1 > min_seconds:
-                            break
-                else:
-                    oracle.decode_attention(w.q, kc, vc, w.block_tables, w.context_lens,
-                                            w.scale, w.dtype, seq_ids=[s])
-                    kv += 2 * int(w.context_lens[s]) * w.num_kv_heads * w.head_dim * b
-                    rows += 1
-                seqs += 1
-                if time.perf_counter() - t1 > min_seconds:
-                    break
-            if time.perf_counter() - t1 > min_seconds:
-                break
-        dt = time.perf_counter() - t1
-    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        r1, s1, kv1 = _oracle_pass({**arrays, **facts}, list(range(w.num_seqs)), one_s)
+        one_rate = kv1 / (time.perf_counter() - t1)
+
+    used, note = 1, ""
+    rate, rows, seqs, dt = one_rate, r1, s1, one_s
+    shms = []
+    try:
+        if workers > 1:
+            spec = {}
+            for name, arr in arrays.items():
+                arr = np.ascontiguousarray(arr)
+                shm = shared_memory.SharedMemory(create=True, size=max(1, arr.nbytes))
+                shms.append(shm)
+                np.ndarray(arr.shape, dtype=arr.dtype, buffer=shm.buf)[...] = arr
+                spec[name] = (shm.name, arr.shape, arr.dtype.str)
+            saved = {k: os.environ.get(k) for k in ("PKV_BENCH_CPU_WORKER", "OMP_NUM_THREADS",
+                                                     "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+            os.environ.update({"PKV_BENCH_CPU_WORKER": "1", "OMP_NUM_THREADS": "1",
+                               "OPENBLAS_NUM_THREADS": "1", "MKL_NUM_THREADS": "1"})
+            try:
+                # a worker that fails to start breaks the pool (an error here),
+                # it is not started again
+                with ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn"),
+                                         initializer=_oracle_worker_init,
+                                         initargs=(spec, facts)) as pool:
+                    list(pool.map(_oracle_worker_run, [(i, workers, 0.0) for i in range(workers)]))
+                    t2 = time.perf_counter()
+                    res = list(pool.map(_oracle_worker_run,
+                                        [(i, workers, min_seconds) for i in range(workers)]))
+                    dt = time.perf_counter() - t2
+            finally:
+                for k, v in saved.items():
+                    if v is None:
+                        os.environ.pop(k, None)
+                    else:
+                        os.environ[k] = v
+            rows = sum(r[0] for r in res)
+            seqs = sum(r[1] for r in res)
+            rate = sum(r[2] for r in res) / dt
+            used = workers
+    except (OSError, BrokenProcessPool) as e:  # no shared memory or processes here
+        note = f"; {workers} worker processes unavailable ({type(e).__name__}), one process"
+    finally:
+        for shm in shms:
+            shm.close()
+            shm.unlink()
+    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
             "sample": (f"{rows} query rows of {seqs} sequence-attentions of this step "
                        f"({seqs / w.num_seqs:.2f} passes over the {w.num_seqs}-sequence batch, "
                        f"the last one possibly in part) after its cache writes "
-                       f"({t1 - t0:.1f} s), fp64 NumPy, one thread, {dt:.1f} s"),
-            "rows_per_s": round(rows / dt, 2)}
+                       f"({t_writes:.1f} s), fp64 NumPy, {used} process(es) of one BLAS thread, "
+                       f"{dt:.1f} s{note}"),
+            "rows_per_s": round(rows / dt, 2),
+            "one_process_GBps": round(one_rate / 1e9, 4)}
 
 
 def block_manager_trace(seed=388008, num_seqs=256, system_tokens=1000, steps=256):
@@ -404,6 +499,9 @@ def main():
                          + ", ".join(wl.MULTI))
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="duration of the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="processes of the CPU oracle baseline (default: the usable cores, "
+                         "at most 16)")
     ap.add_argument("--read-probe-mib", type=int, default=0,
                     help="instead of the decode step, time pkv_stream_read of this many MiB "
                          "(the achievable read-bandwidth reference)")
@@ -445,7 +543,8 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, args.cpu_seconds)
+        workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
+        cpu = cpu_baseline(w, args.cpu_seconds, workers)
         print(f"[bench] cpu oracle: {cpu['sample']}", file=sys.stderr, flush=True)
 
     import torch
