@@ -1446,10 +1446,27 @@ void attn_prefill_kernel(AttnParams prm) {
   const int lane = tid & 63;
   const int w = uniform(tid >> 6);
   const int r = lane >> 4;
-  const int h = (int)blockIdx.y;
+  // Workgroups are dispatched in linear id order, id i to XCD i % 8.  Inside
+  // one grid row z (one sequence, kept in its dispatch slot) the ids are
+  // dealt so that each (kv head, part) unit goes whole to one XCD, its column
+  // blocks one after another: they read the same K/V, which then stays in
+  // that XCD's L2.  (Otherwise the ids of the unit's column blocks, being
+  // consecutive, landed on every XCD.)
   const int P = prm.prefill_parts;
-  const int cb = (int)blockIdx.x / P;
-  const int part = (int)blockIdx.x % P;
+  const int U = P * (int)gridDim.y;   // units per row
+  const int nb = (int)gridDim.x / P;  // column blocks
+  const int wrow = (int)blockIdx.x + (int)gridDim.x * (int)blockIdx.y;
+  int u, cb;
+  if (U % kXcds == 0) {
+    const int j = wrow / kXcds;
+    u = wrow % kXcds + kXcds * (j / nb);
+    cb = j % nb;
+  } else {
+    u = (int)blockIdx.y * P + (int)blockIdx.x % P;
+    cb = (int)blockIdx.x / P;
+  }
+  const int h = u / P;
+  const int part = u % P;
   const int G = prm.group;
   const int Hq = prm.num_q_heads;
 
