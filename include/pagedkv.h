@@ -52,10 +52,31 @@ typedef enum {
   PKV_EUNSUPPORTED = 2,  /* valid but not built: head_dim, block_size, dtype, group */
   PKV_EWORKSPACE = 3,    /* workspace missing or smaller than required */
   PKV_EHIP = 4,          /* a HIP runtime call or kernel launch failed */
-  PKV_ECHECK = 5         /* reserved for metadata validation failures */
+  PKV_ECHECK = 5         /* metadata check failed (PAGEDKV_CHECK=1, see below) */
 } pkv_status;
 
 typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+/*
+ * Metadata check mode.  Device metadata (block tables, context lengths,
+ * query starts, slots, copy pairs, swap ids) is trusted: a bad entry never
+ * moves an access outside its buffer, but the result is then undefined.
+ * With the environment variable PAGEDKV_CHECK=1 every entry point first
+ * copies its metadata to the host on its stream, waits for it, and returns
+ * PKV_ECHECK (nothing enqueued, pkv_last_error naming the entry) for:
+ *  - attention: context_lens[s] outside [0, max_context_len]; a block id a
+ *    context uses (entries j < ceil(n / block_size)) outside the pool;
+ *    query_start not starting at 0, not ending at num_query_tokens, or
+ *    giving a sequence a negative count of new tokens or more than
+ *    min(n, max_query_len);
+ *  - paged_kv_append: a slot at or past num_blocks * block_size, or one slot
+ *    written twice (negative slots are skipped);
+ *  - paged_copy_blocks: a block id outside the pool, a destination named
+ *    twice, or a destination that is also a source;
+ *  - swaps: a block id outside the pool or named twice.
+ * Debug only: the wait costs a round trip per call, and under stream
+ * capture (where waiting is not allowed) the calls return PKV_EUNSUPPORTED.
+ */
 
 /* Shape of the K and V pools (they share it). */
 typedef struct {

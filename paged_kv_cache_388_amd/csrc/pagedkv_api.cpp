@@ -5,8 +5,11 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
+#include <algorithm>
 #include <atomic>
+#include <vector>
 
 #include <hip/hip_runtime_api.h>
 
@@ -29,6 +32,50 @@ pkv_status hip_fail(hipError_t err, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---- metadata check mode -----------------------------------------------------
+// Device metadata (block tables, lengths, slots, pairs) is trusted: the
+// kernels never let a bad entry move an access outside its buffer, but the
+// result is then undefined.  With PAGEDKV_CHECK=1 in the environment each
+// entry point first copies its metadata to the host (on its stream, then
+// waits for it) and rejects what breaks the contract with PKV_ECHECK.  Debug
+// only: the wait is not allowed while the stream is being captured.
+
+bool check_mode() {
+  const char* v = getenv("PAGEDKV_CHECK");
+  return v && v[0] == '1' && v[1] == '\0';
+}
+
+pkv_status fetch_i32(std::vector<int32_t>& h, const int32_t* d, size_t count, hipStream_t stream,
+                     const char* what) {
+  h.assign(count, 0);
+  if (count == 0) return PKV_OK;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone)
+    return fail(PKV_EUNSUPPORTED, "%s: PAGEDKV_CHECK=1 waits for the stream, which capture forbids",
+                what);
+  hipError_t err = hipMemcpyAsync(h.data(), d, count * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (err == hipSuccess) err = hipStreamSynchronize(stream);
+  return err == hipSuccess ? PKV_OK : hip_fail(err, what);
+}
+
+// ids[0..n) inside [0, num_blocks) and, if `unique`, pairwise distinct
+pkv_status check_ids(const char* what, const char* name, const std::vector<int32_t>& ids,
+                     size_t stride, size_t offset, int32_t num_blocks, bool unique) {
+  std::vector<int32_t> seen;
+  for (size_t i = offset; i < ids.size(); i += stride) {
+    const int32_t id = ids[i];
+    if (id < 0 || id >= num_blocks)
+      return fail(PKV_ECHECK, "%s: %s entry %zu = %d is outside the pool [0, %d)", what, name,
+                  (i - offset) / stride, id, num_blocks);
+    if (unique) seen.push_back(id);
+  }
+  std::sort(seen.begin(), seen.end());
+  for (size_t i = 1; i < seen.size(); ++i)
+    if (seen[i] == seen[i - 1])
+      return fail(PKV_ECHECK, "%s: %s names block %d more than once", what, name, seen[i]);
+  return PKV_OK;
+}
 
 int elem_bytes(int32_t dtype) {
   switch (dtype) {
@@ -139,6 +186,23 @@ pkv_status paged_kv_append(const void* key, const void* value, void* k_cache, vo
     return fail(PKV_EINVAL, "key, value and the pools must be 16-byte aligned");
   if ((long long)pool.num_blocks * pool.block_size > 0x7fffffffLL)
     return fail(PKV_EINVAL, "num_blocks * block_size exceeds the int32 slot range");
+  if (check_mode()) {
+    std::vector<int32_t> slots;
+    st = fetch_i32(slots, slot_mapping, (size_t)num_tokens, stream, "paged_kv_append check");
+    if (st != PKV_OK) return st;
+    const int32_t nslots = pool.num_blocks * pool.block_size;
+    std::vector<int32_t> used;
+    for (int32_t i = 0; i < num_tokens; ++i) {
+      if (slots[i] >= nslots)
+        return fail(PKV_ECHECK, "paged_kv_append: slot_mapping[%d] = %d is outside the pool's %d slots",
+                    i, slots[i], nslots);
+      if (slots[i] >= 0) used.push_back(slots[i]);
+    }
+    std::sort(used.begin(), used.end());
+    for (size_t i = 1; i < used.size(); ++i)
+      if (used[i] == used[i - 1])
+        return fail(PKV_ECHECK, "paged_kv_append: slot %d is written more than once", used[i]);
+  }
   hipError_t err = pkv::launch_kv_append(key, value, k_cache, v_cache, slot_mapping, num_tokens,
                                          pool.num_kv_heads, pool.block_size, pool.head_dim,
                                          elem_bytes(pool.dtype), pool.num_blocks, stream);
@@ -232,6 +296,39 @@ pkv_status attention_call(const char* what, void* out, const void* q, const void
     return fail(PKV_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, lay.bytes);
   if (lay.bytes > 0 && !aligned16(workspace)) return fail(PKV_EINVAL, "workspace must be 16-byte aligned");
 
+  if (check_mode()) {
+    std::vector<int32_t> lens, tables, qs;
+    st = fetch_i32(lens, context_lens, (size_t)num_seqs, stream, what);
+    if (st == PKV_OK && max_blocks_per_seq > 0)
+      st = fetch_i32(tables, block_tables, (size_t)num_seqs * max_blocks_per_seq, stream, what);
+    if (st == PKV_OK && multi) st = fetch_i32(qs, query_start, (size_t)num_seqs + 1, stream, what);
+    if (st != PKV_OK) return st;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      const int32_t n = lens[s];
+      if (n < 0 || n > max_context_len)
+        return fail(PKV_ECHECK, "context_lens[%d] = %d is outside [0, max_context_len %d]", s, n,
+                    max_context_len);
+      const int32_t nb = (n + pool.block_size - 1) / pool.block_size;
+      for (int32_t j = 0; j < nb; ++j) {
+        const int32_t id = tables[(size_t)s * max_blocks_per_seq + j];
+        if (id < 0 || id >= pool.num_blocks)
+          return fail(PKV_ECHECK, "block_tables[%d][%d] = %d is outside the pool [0, %d)", s, j, id,
+                      pool.num_blocks);
+      }
+      if (multi) {
+        const int32_t L = qs[s + 1] - qs[s];
+        if (qs[s] < 0 || L < 0 || L > n || L > max_query_len)
+          return fail(PKV_ECHECK,
+                      "query_start[%d..%d] = %d..%d: %d new tokens, with a context of %d and "
+                      "max_query_len %d",
+                      s, s + 1, qs[s], qs[s + 1], L, n, max_query_len);
+      }
+    }
+    if (multi && (qs[0] != 0 || qs[num_seqs] != num_query_tokens))
+      return fail(PKV_ECHECK, "query_start runs from %d to %d, not from 0 to num_query_tokens %d",
+                  qs[0], qs[num_seqs], num_query_tokens);
+  }
+
   pkv::AttnParams prm;
   prm.out = out;
   prm.q = q;
@@ -318,6 +415,20 @@ pkv_status paged_copy_blocks(void* k_cache, void* v_cache, pkv_pool pool,
   if (!k_cache || !v_cache || !block_mapping) return fail(PKV_EINVAL, "null pointer argument");
   if (!aligned16(k_cache) || !aligned16(v_cache)) return fail(PKV_EINVAL, "pools must be 16-byte aligned");
   if (num_pairs > 0x3fffffff) return fail(PKV_EINVAL, "num_pairs %d too large", num_pairs);
+  if (check_mode()) {
+    std::vector<int32_t> pairs;
+    st = fetch_i32(pairs, block_mapping, (size_t)num_pairs * 2, stream, "paged_copy_blocks check");
+    if (st == PKV_OK) st = check_ids("paged_copy_blocks", "block_mapping src", pairs, 2, 0, pool.num_blocks, false);
+    if (st == PKV_OK) st = check_ids("paged_copy_blocks", "block_mapping dst", pairs, 2, 1, pool.num_blocks, true);
+    if (st != PKV_OK) return st;
+    std::vector<int32_t> srcs;
+    for (int32_t i = 0; i < num_pairs; ++i) srcs.push_back(pairs[2 * i]);
+    std::sort(srcs.begin(), srcs.end());
+    for (int32_t i = 0; i < num_pairs; ++i)
+      if (std::binary_search(srcs.begin(), srcs.end(), pairs[2 * i + 1]))
+        return fail(PKV_ECHECK, "paged_copy_blocks: block %d is both a destination and a source",
+                    pairs[2 * i + 1]);
+  }
   hipError_t err = pkv::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs,
                                            pool_block_bytes(pool), pool.num_blocks, stream);
   return err == hipSuccess ? PKV_OK : hip_fail(err, "paged_copy_blocks launch");
@@ -357,6 +468,12 @@ pkv_status paged_swap_out(const void* k_cache, const void* v_cache, pkv_pool poo
   pkv_status st = swap_check("paged_swap_out", k_cache, v_cache, pool, block_ids, num_ids,
                              host_image, staging, staging_bytes, &per_run);
   if (st != PKV_OK || num_ids == 0) return st;
+  if (check_mode()) {
+    std::vector<int32_t> ids;
+    st = fetch_i32(ids, block_ids, (size_t)num_ids, stream, "paged_swap_out check");
+    if (st == PKV_OK) st = check_ids("paged_swap_out", "block_ids", ids, 1, 0, pool.num_blocks, true);
+    if (st != PKV_OK) return st;
+  }
   const size_t bb = pool_block_bytes(pool);
   for (int32_t start = 0; start < num_ids; start += per_run) {
     const int32_t cnt = num_ids - start < per_run ? num_ids - start : per_run;
@@ -378,6 +495,12 @@ pkv_status paged_swap_in(const void* host_image, int32_t num_ids, void* k_cache,
   pkv_status st = swap_check("paged_swap_in", k_cache, v_cache, pool, block_ids, num_ids,
                              host_image, staging, staging_bytes, &per_run);
   if (st != PKV_OK || num_ids == 0) return st;
+  if (check_mode()) {
+    std::vector<int32_t> ids;
+    st = fetch_i32(ids, block_ids, (size_t)num_ids, stream, "paged_swap_in check");
+    if (st == PKV_OK) st = check_ids("paged_swap_in", "block_ids", ids, 1, 0, pool.num_blocks, true);
+    if (st != PKV_OK) return st;
+  }
   const size_t bb = pool_block_bytes(pool);
   for (int32_t start = 0; start < num_ids; start += per_run) {
     const int32_t cnt = num_ids - start < per_run ? num_ids - start : per_run;
