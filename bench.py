@@ -508,6 +508,9 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="write a 1 GiB scrub buffer before every timed step, so that no "
                          "K/V byte is served from L2 or the Infinity Cache")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step as one captured HIP graph (the attention call's "
+                         "events are then taken in a loop of their own)")
     ap.add_argument("--swap", action="store_true",
                     help="instead of the decode step, time swap out / in of a preempted batch")
     ap.add_argument("--block-manager", action="store_true",
@@ -517,6 +520,8 @@ def main():
                     help="instead of the decode step, time pkv_stream_copy of this many MiB "
                          "(the reference copy for bandwidth and HBM counter calibration)")
     args = ap.parse_args()
+    if args.graph and args.cold:
+        ap.error("--graph and --cold exclude each other (the scrub is not part of the step)")
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
@@ -604,17 +609,39 @@ def main():
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if scrub is not None:
-            scrub.fill_(i & 0xff)
-            wstarts[i].record(stream)
-        write_step()
-        starts[i].record(stream)
-        attend()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    if args.graph:
+        # the step (cache writes + attention) captured once as a HIP graph and
+        # replayed: one launch per step instead of one per kernel
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            write_step()
+            attend()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        # the attention call alone, for its events (roofline)
+        for i in range(args.steps):
+            starts[i].record(stream)
+            attend()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+    else:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            if scrub is not None:
+                scrub.fill_(i & 0xff)
+                wstarts[i].record(stream)
+            write_step()
+            starts[i].record(stream)
+            attend()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     if scrub is None:
         # the cache writes alone, outside the timed region (an extra event per
         # step inside it would lengthen the step it measures); they rewrite
@@ -710,7 +737,8 @@ def main():
                    "step": ("copy_blocks + paged_kv_append + "
                             + ("paged_attention_multi" if w.multi else "paged_attention_decode")),
                    "new_tokens": int(w.q.shape[0]),
-                   "parallelism": "single GPU", "cold": bool(args.cold)},
+                   "parallelism": "single GPU", "cold": bool(args.cold),
+                   "graph": bool(args.graph)},
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "seqs_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "new_tokens_per_s": round(w.q.shape[0] / (ms_per_step * 1e-3), 1),
