@@ -340,20 +340,24 @@ __device__ __forceinline__ void attend_core(const uint4 (&ka)[N], const uint32_t
 // taken as tokens 4r .. 4r+3 of the first sub-tile, then of the second.
 // That is exactly what each lane holds of P (its QK outputs) and of V (its
 // loaded rows), so no operand moves between lanes; A and B only need to
-// agree on it.  V comes pre-arranged (va[wd] = the four A-operand words of
-// head-dim pair wd: rows 0-1 and 2-3 of the even dim, then of the odd one).
+// agree on it.  V comes as the A operands themselves: ve[wd] / vo[wd] hold
+// head dim 2 wd / 2 wd + 1 at the lane's four rows of the first sub-tile,
+// then its four rows of the second (two bf16/f16 per word).
 //
 // The softmax reference max is updated lazily: a column keeps its reference
 // m while its new logits stay within kLazyLog2 of it (its p stay <= 2^8), and
 // the accumulators are rescaled only when some column of the wave moves its
 // reference.  o = acc / l holds for any reference, so this changes rounding
-// only.  MASK = false when every real column sees all 32 tokens.
+// only.  mask (wave-uniform) = false when every real column sees all 32
+// tokens; it selects only the logits, so both cases share one instruction
+// stream and the accumulators stay in their registers (a separate copy of
+// the pair per case made the compiler move all of them at every join).
 constexpr float kLazyLog2 = 8.f;
 
-template <int DT, int N, int kMM, bool MASK>
+template <int DT, int N, int kMM>
 __device__ __forceinline__ void attend_pair(const uint4 (&ka0)[N], const uint4 (&ka1)[N],
-                                            const u32x4 (&va0)[N], const u32x4 (&va1)[N],
-                                            const uint4 (&qb)[N], int valid0, int valid1,
+                                            const u32x4 (&ve)[N], const u32x4 (&vo)[N],
+                                            const uint4 (&qb)[N], bool mask, int valid0, int valid1,
                                             float scale_log2, int r, WaveState<kMM>& st) {
   static_assert(DT != DT_F32, "16-bit types only");
   floatx4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
@@ -376,7 +380,10 @@ __device__ __forceinline__ void attend_pair(const uint4 (&ka0)[N], const uint4 (
   for (int e = 0; e < 4; ++e) {
     sv[e] = S0[e] * scale_log2;
     sv[4 + e] = S1[e] * scale_log2;
-    if constexpr (MASK) {
+  }
+  if (mask) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
       sv[e] = (4 * r + e < valid0) ? sv[e] : kNegInf;
       sv[4 + e] = (4 * r + e < valid1) ? sv[4 + e] : kNegInf;
     }
@@ -420,8 +427,7 @@ __device__ __forceinline__ void attend_pair(const uint4 (&ka0)[N], const uint4 (
   static_assert(kMM == 2 * N, "16-bit types: two head-dim rows per V word");
 #pragma unroll
   for (int wd = 0; wd < N; ++wd) {
-    const u32x4 ae = __builtin_shufflevector(va0[wd], va1[wd], 0, 1, 4, 5);  // row 2 wd
-    const u32x4 ao = __builtin_shufflevector(va0[wd], va1[wd], 2, 3, 6, 7);  // row 2 wd + 1
+    const u32x4 ae = ve[wd], ao = vo[wd];  // rows 2 wd and 2 wd + 1 of V^T
     if constexpr (DT == DT_BF16) {
       const bf16x8 hi = __builtin_bit_cast(bf16x8, phi), lo = __builtin_bit_cast(bf16x8, plo);
       const bf16x8 Ae = __builtin_bit_cast(bf16x8, ae), Ao = __builtin_bit_cast(bf16x8, ao);
@@ -1574,16 +1580,24 @@ void attn_prefill_kernel(AttnParams prm) {
     }
 #pragma unroll
     for (int qd = 0; qd < N; ++qd) {
-      uint4 x;
       if constexpr (DT == DT_F32) {
-        x = make_uint4(t.v[0][qd], t.v[1][qd], t.v[2][qd], t.v[3][qd]);
-      } else {  // the PV A-operand words of dim pair qd (attend_pair's va)
-        x.x = __builtin_amdgcn_perm(t.v[1][qd], t.v[0][qd], 0x05040100u);
-        x.y = __builtin_amdgcn_perm(t.v[3][qd], t.v[2][qd], 0x05040100u);
-        x.z = __builtin_amdgcn_perm(t.v[1][qd], t.v[0][qd], 0x07060302u);
-        x.w = __builtin_amdgcn_perm(t.v[3][qd], t.v[2][qd], 0x07060302u);
+        *reinterpret_cast<uint4*>(&sV[b][w][(qd * 64 + lane) * 16]) =
+            make_uint4(t.v[0][qd], t.v[1][qd], t.v[2][qd], t.v[3][qd]);
+      } else {
+        // The PV A-operand words of dim pair qd: even dim at rows 0-1, 2-3,
+        // odd dim likewise.  Sub-tiles 2p and 2p + 1 of a stage form pair p,
+        // whose two slots hold, per (qd, even/odd, lane), the first
+        // sub-tile's two words then the second's: attend_pair reads each
+        // operand with one load.
+        uint2 ev, od;
+        ev.x = __builtin_amdgcn_perm(t.v[1][qd], t.v[0][qd], 0x05040100u);
+        ev.y = __builtin_amdgcn_perm(t.v[3][qd], t.v[2][qd], 0x05040100u);
+        od.x = __builtin_amdgcn_perm(t.v[1][qd], t.v[0][qd], 0x07060302u);
+        od.y = __builtin_amdgcn_perm(t.v[3][qd], t.v[2][qd], 0x07060302u);
+        char* pair = &sV[b][w & ~1][0] + 8 * (w & 1);
+        *reinterpret_cast<uint2*>(pair + ((2 * qd) * 64 + lane) * 16) = ev;
+        *reinterpret_cast<uint2*>(pair + ((2 * qd + 1) * 64 + lane) * 16) = od;
       }
-      *reinterpret_cast<uint4*>(&sV[b][w][(qd * 64 + lane) * 16]) = x;
     }
   };
 
@@ -1603,6 +1617,15 @@ void attn_prefill_kernel(AttnParams prm) {
 #pragma unroll
     for (int qd = 0; qd < N; ++qd) va[qd] = *reinterpret_cast<const u32x4*>(&sV[b][j][(qd * 64 + lane) * 16]);
   };
+  // V operands of pair p (sub-tiles 2p, 2p + 1), as park lays them out
+  auto fetch_v_pair = [&](u32x4 (&ve)[N], u32x4 (&vo)[N], int b, int p) {
+    const char* pair = &sV[b][2 * p][0];
+#pragma unroll
+    for (int qd = 0; qd < N; ++qd) {
+      ve[qd] = *reinterpret_cast<const u32x4*>(pair + ((2 * qd) * 64 + lane) * 16);
+      vo[qd] = *reinterpret_cast<const u32x4*>(pair + ((2 * qd + 1) * 64 + lane) * 16);
+    }
+  };
   auto valid_of = [&](int sub) {
     const int v = vis - sub * kSub;
     return v > kSub ? kSub : v;
@@ -1620,16 +1643,13 @@ void attn_prefill_kernel(AttnParams prm) {
         const int sub = sg * kWaves + j;
         if (sub < nsub_w) {
           uint4 ka0[N], ka1[N];
-          u32x4 va0[N], va1[N];
+          u32x4 ve[N], vo[N];
           fetch_k(ka0, b, j);
           fetch_k(ka1, b, j + 1);
-          fetch_v(va0, b, j);
-          fetch_v(va1, b, j + 1);
-          if ((sub + 2) * kSub <= vis_first)
-            attend_pair<DT, N, kMM, false>(ka0, ka1, va0, va1, qb, kSub, kSub, scale_log2, r, st);
-          else
-            attend_pair<DT, N, kMM, true>(ka0, ka1, va0, va1, qb, valid_of(sub), valid_of(sub + 1),
-                                          scale_log2, r, st);
+          fetch_v_pair(ve, vo, b, j / 2);
+          const bool mask = (sub + 2) * kSub > vis_first;
+          attend_pair<DT, N, kMM>(ka0, ka1, ve, vo, qb, mask, valid_of(sub), valid_of(sub + 1),
+                                  scale_log2, r, st);
         }
       }
     } else {
