@@ -1437,7 +1437,7 @@ __global__ __launch_bounds__(64) void attn_stream_merge_group_kernel(AttnParams 
 // blocks past a sequence's columns, and empty parts, exit at once.
 
 template <int DT, int D, int BS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void attn_prefill_kernel(AttnParams prm) {
   using Geo = Geometry<DT, D, BS>;
   constexpr int N = Geo::N;
@@ -1445,8 +1445,8 @@ void attn_prefill_kernel(AttnParams prm) {
   constexpr int kRow = Geo::kRow;
   constexpr int kSubBytes = kSub * kRow;
   constexpr int kSwz = (4 * N - 1) < 15 ? (4 * N - 1) : 15;
-  __shared__ __attribute__((aligned(16))) char sK[2][kWaves][kSubBytes];
-  __shared__ __attribute__((aligned(16))) char sV[2][kWaves][kSubBytes];
+  __shared__ __attribute__((aligned(16))) char sK[1][kWaves][kSubBytes];
+  __shared__ __attribute__((aligned(16))) char sV[1][kWaves][kSubBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1684,12 +1684,13 @@ void attn_prefill_kernel(AttnParams prm) {
   park(t, 0);
   __syncthreads();
   for (int sg = st0; sg < st1; ++sg) {
-    const int b = (sg - st0) & 1;
     load_sub(t, (sg + 1) * kWaves + w);
-    compute_stage(sg, b);
-    park(t, b ^ 1);
+    compute_stage(sg, 0);
+    __syncthreads();  // every wave has read the stage
+    park(t, 0);
     __syncthreads();
   }
+
 
   if (cg < ngrp) {
     float l = st.l + __shfl_xor(st.l, 16);
