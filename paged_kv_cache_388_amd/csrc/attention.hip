@@ -354,6 +354,20 @@ __device__ __forceinline__ void attend_core(const uint4 (&ka)[N], const uint32_t
 // the pair per case made the compiler move all of them at every join).
 constexpr float kLazyLog2 = 8.f;
 
+// Maximum of x over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four row groups
+// of one MFMA column): two row swaps (v_permlane16_swap, v_permlane32_swap),
+// each one VALU instruction with no LDS round trip.  The NaN-propagating
+// maximum needs no quieting of its inputs (fmaxf's NaN rules make the
+// compiler add one instruction per operand); logits are finite here.
+__device__ __forceinline__ float rows_max(float x) {
+  unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  u = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <int DT, int N, int kMM>
 __device__ __forceinline__ void attend_pair(const uint4 (&ka0)[N], const uint4 (&ka1)[N],
                                             const u32x4 (&ve)[N], const u32x4 (&vo)[N],
@@ -388,10 +402,8 @@ __device__ __forceinline__ void attend_pair(const uint4 (&ka0)[N], const uint4 (
       sv[4 + e] = (4 * r + e < valid1) ? sv[4 + e] : kNegInf;
     }
   }
-  float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  const auto mx = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+  const float mloc = rows_max(mx(mx(mx(sv[0], sv[1]), mx(sv[2], sv[3])), mx(mx(sv[4], sv[5]), mx(sv[6], sv[7]))));
   const bool move = mloc > st.m + kLazyLog2;  // -inf > -inf is false: a fully masked column stays
   if (__builtin_amdgcn_ballot_w64(move)) {
     const float m_new = move ? mloc : st.m;
