@@ -389,11 +389,16 @@ __device__ __forceinline__ void attend_pair(const uint4 (&ka0)[N], const uint4 (
                                                    __builtin_bit_cast(bf16x8, qb[kk]), S1, 0, 0, 0);
     }
   }
+  // Raw scores S; the logit is c * S with c = scale_log2 > 0 (a negative
+  // scale arrives as a negated query, a zero one as the smallest normal
+  // float).  Multiplying by c > 0 is monotone in floating point, so the
+  // largest logit is exactly c * max S, and each exponent is one fma,
+  // exp2(c * S - m); a masked score is -inf and gets weight 0.
   float sv[8];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    sv[e] = S0[e] * scale_log2;
-    sv[4 + e] = S1[e] * scale_log2;
+    sv[e] = S0[e];
+    sv[4 + e] = S1[e];
   }
   if (mask) {
 #pragma unroll
@@ -403,7 +408,8 @@ __device__ __forceinline__ void attend_pair(const uint4 (&ka0)[N], const uint4 (
     }
   }
   const auto mx = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
-  const float mloc = rows_max(mx(mx(mx(sv[0], sv[1]), mx(sv[2], sv[3])), mx(mx(sv[4], sv[5]), mx(sv[6], sv[7]))));
+  const float mloc =
+      scale_log2 * rows_max(mx(mx(mx(sv[0], sv[1]), mx(sv[2], sv[3])), mx(mx(sv[4], sv[5]), mx(sv[6], sv[7]))));
   const bool move = mloc > st.m + kLazyLog2;  // -inf > -inf is false: a fully masked column stays
   if (__builtin_amdgcn_ballot_w64(move)) {
     const float m_new = move ? mloc : st.m;
@@ -413,10 +419,10 @@ __device__ __forceinline__ void attend_pair(const uint4 (&ka0)[N], const uint4 (
     for (int mm = 0; mm < kMM; ++mm) st.acc[mm] *= alpha;
     st.m = m_new;
   }
-  const float mb = st.m == kNegInf ? 0.f : st.m;
+  const float nmb = st.m == kNegInf ? 0.f : -st.m;
   float pe[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(sv[e] - mb);
+  for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(__builtin_fmaf(sv[e], scale_log2, nmb));
   st.l += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
 
   uint4 phi, plo;
@@ -1534,6 +1540,18 @@ void attn_prefill_kernel(AttnParams prm) {
   const int cg = cb * kWaves + w;
   uint4 qb[N];
   load_query_cols<N, true>(qb, prm.q, sc, h, cg, G, Hq, lane);
+  // 16-bit types: the core takes a non-negative logit scale; a negative one
+  // becomes a negated query (a sign flip, exact)
+  const bool neg_scale = prm.scale_log2 < 0.f;
+  if constexpr (DT != DT_F32)
+    if (neg_scale)
+#pragma unroll
+      for (int kk = 0; kk < N; ++kk) {
+        qb[kk].x ^= 0x80008000u;
+        qb[kk].y ^= 0x80008000u;
+        qb[kk].z ^= 0x80008000u;
+        qb[kk].w ^= 0x80008000u;
+      }
   const int col = cg * kSub + (lane & 15);
   const int vis = col < L * G ? n - L + col / G + 1 : 0;  // tokens this lane's column sees
   // tokens the last column of this wave's group / of the block's last group sees
@@ -1615,7 +1633,13 @@ void attn_prefill_kernel(AttnParams prm) {
 
   WaveState<kMM> st;
   st.reset();
-  const float scale_log2 = prm.scale_log2;
+  // fp32 scales its logits directly.  16-bit types take |scale| (see above),
+  // and a zero scale as the smallest normal float: every logit c * S is then
+  // within 2^-24 of zero for |S| < 2^100, so every weight exp2(c * S - m)
+  // rounds to exactly 1 as it would for c = 0, while a masked -inf stays -inf.
+  float scale_log2 = DT != DT_F32 && neg_scale ? -prm.scale_log2 : prm.scale_log2;
+  if constexpr (DT != DT_F32)
+    if (scale_log2 == 0.f) scale_log2 = 1.17549435e-38f;
   // QK, softmax and PV over the four sub-tiles of stage sg (LDS buffer b).
   auto fetch_k = [&](uint4 (&ka)[N], int b, int j) {
     const int tr = lane & 15;

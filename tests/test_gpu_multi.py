@@ -51,6 +51,24 @@ def test_multi_other_groups(G):
     _run(w, f"multi G{G}")
 
 
+@pytest.mark.parametrize("mult", [-1.0, 0.0, 3.0])
+@pytest.mark.parametrize("path,dtype", [("decode", "bf16"), ("stream", "bf16"), ("prefill", "bf16"),
+                                        ("prefill", "f16")])
+def test_scale_negative_zero_and_large(path, dtype, mult):
+    """The logit scale is a caller argument of any sign: a negative scale
+    attends by the negated scores, a zero scale weighs every visible token
+    equally, a large one peaks the softmax.  Decode, the multi-token stream
+    path (L * G <= 16) and the prefill path (L * G >= 64) against the oracle."""
+    rng = np.random.default_rng(60)
+    ctx = [1, 17, 300, 700]
+    qlens = {"decode": None, "stream": [1, 3, 4, 2], "prefill": [1, 17, 32, 20]}[path]
+    w = wl.build(f"scale_{path}_{mult}", 60, rng, ctx, 8, 2, 128, 16, dtype,
+                 scale=mult / np.sqrt(128), poison=True, query_lens=qlens)
+    if path == "prefill":
+        assert w.max_query_len * 4 >= 64
+    _run(w, f"{path} {dtype} scale {mult}/sqrt(D)")
+
+
 def test_whole_context_chunks():
     rng = np.random.default_rng(43)
     ctx = [1, 16, 33, 64]
