@@ -6,7 +6,10 @@ new tokens' K/V into their slots) followed by paged decode attention.  The
 default workload is the Llama-3-8B-shaped GQA layer: 128 sequences, 32 query
 / 8 KV heads of 128, bf16, 16-token blocks, contexts log-uniform in
 [256, 8192], shuffled physical pool.  Inputs are seeded and synthetic and are
-resident in HBM before timing starts.
+resident in HBM before timing starts.  Before the warmup steps the attention
+call runs untimed for --settle-ms (200 ms): the GPU idles during the host-side
+setup and its clocks take tens of milliseconds of load to come back up, which
+a handful of warmup steps of a 0.1 ms call does not cover.
 
 Prints ONE JSON line.  ``value`` is the KV bytes a step reads (each cached
 token's K and V once) divided by the measured step time, in GB/s.
@@ -494,6 +497,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed attention calls for this long before the warmup steps: "
+                         "after the host-side setup the GPU has idled, and its clocks take "
+                         "tens of milliseconds of load to ramp up")
     ap.add_argument("--workload", default="llama3_8b_gqa",
                     help="one of: " + ", ".join(wl.NAMED[:4]) + ", long_ctx_bs16, long_ctx_bs32, "
                          + ", ".join(wl.MULTI))
@@ -597,6 +604,12 @@ def main():
             _lib.paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
                                         w.scale, max_ctx, workspace)
 
+    # clock settle (see --settle-ms), in batches of calls between waits
+    t_settle = time.perf_counter() + args.settle_ms * 1e-3
+    while time.perf_counter() < t_settle:
+        for _ in range(20):
+            attend()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         write_step()
         attend()
@@ -723,6 +736,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
