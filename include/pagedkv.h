@@ -176,9 +176,9 @@ PKV_API pkv_status paged_attention_decode(void* out, const void* q,
  * Bytes of workspace paged_attention_multi needs for this shape on the
  * current device, or 0 for invalid input, for a call it refuses, or for a
  * prefill-path call (max_query_len * G >= 64) that keeps each context whole.
- * A prefill-path call with fewer than 1024 (sequence, kv head, 64-column
- * block) workgroups cuts contexts into parts and needs room for the parts'
- * states: num_seqs * max_query_len rows are assumed.
+ * A prefill-path call with fewer than 512 (sequence, kv head, column block)
+ * workgroups cuts contexts into parts and needs room for the parts' states:
+ * num_seqs * max_query_len rows are assumed.
  */
 PKV_API size_t paged_attention_multi_workspace_bytes(pkv_pool pool, int32_t num_seqs,
                                                      int32_t num_q_heads, int32_t max_query_len,
@@ -206,12 +206,15 @@ PKV_API size_t paged_attention_multi_workspace_bytes(pkv_pool pool, int32_t num_
  *    K/V byte once), partial states merged afterwards; num_seqs <= 2048,
  *    at most 2^28 positions (kv heads x column groups x 16-token sub-tiles);
  *  - max_query_len * G >= 64 (prompt chunks): one workgroup per (sequence,
- *    kv head, four column groups) streams the context once through LDS for
- *    64 columns and writes its rows directly; num_seqs <= 65535; up to 256
- *    sequences are dispatched longest context first.  When that gives fewer
- *    than 1024 workgroups, each context is cut into up to 16 parts of at
- *    least 512 tokens, one workgroup each, whose states are merged in part
- *    order afterwards (workspace needed, deterministic as above).
+ *    kv head, column block) streams the context once through LDS for the
+ *    block's columns and writes its rows directly; num_seqs <= 65535; up to
+ *    256 sequences are dispatched longest context first.  A block is eight
+ *    16-column groups (two per wave) for 16-bit types where the call has at
+ *    least 1024 such workgroups or fewer than 512, else four (one per wave);
+ *    fp32 always four.  When a call has fewer than 512 workgroups, each
+ *    context is cut into up to 16 parts of at least 512 tokens, one
+ *    workgroup each, whose states are merged in part order afterwards
+ *    (workspace needed, deterministic as above).
  * Both give the same result up to fp32 rounding order.  Precision,
  * determinism and metadata trust as for paged_attention_decode; rows of a
  * sequence are clamped to [0, num_query_tokens] and to at most

@@ -1441,22 +1441,24 @@ __global__ __launch_bounds__(64) void attn_stream_merge_group_kernel(AttnParams 
 //
 // With L new tokens a sequence has ceil(L * G / 16) column groups; the stream
 // kernel streams its context once per group, so a 256-token chunk at G = 4
-// reads every K/V byte 64 times.  Here a workgroup takes four consecutive
-// column groups of one (sequence, kv head), one per wave, and streams the
-// context once for all four: per stage each wave loads one 16-token sub-tile
-// (the block table row read with scalar loads), parks it in LDS (K in the
-// A-operand staging order, V in its load order), and after a barrier every
-// wave runs QK, online softmax and PV over the stage's four sub-tiles for its
-// own 16 columns.  The next stage's loads are in flight meanwhile.  A
+// reads every K/V byte 64 times.  Here a workgroup takes 4 * GW consecutive
+// column groups of one (sequence, kv head), GW per wave, and streams the
+// context once for all of them: per stage each wave loads one 16-token
+// sub-tile (the block table row read with scalar loads) and parks it in LDS
+// (K in the A-operand staging order, V as the PV A operands), and after a
+// barrier every wave runs QK, online softmax and PV over the stage's four
+// sub-tiles for its own 16 * GW columns, each K/V operand it reads serving
+// all of its groups.  The next stage's loads are in flight meanwhile.  A
 // workgroup that covers the whole context writes the output rows directly;
 // when a call has too few workgroups to fill the chip, each context is cut
 // into stage-aligned parts, one workgroup each, and a merge combines the
 // parts' states.  Grid: (column block, part) x kv head x sequence rank;
 // blocks past a sequence's columns, and empty parts, exit at once.
 
-template <int DT, int D, int BS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+template <int DT, int D, int BS, int GW>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GW == 2 ? 2 : 3)))
 void attn_prefill_kernel(AttnParams prm) {
+  static_assert(GW == 1 || (GW == 2 && DT != DT_F32), "two groups per wave: 16-bit types");
   using Geo = Geometry<DT, D, BS>;
   constexpr int N = Geo::N;
   constexpr int kMM = Geo::kMM;
@@ -1530,38 +1532,52 @@ void attn_prefill_kernel(AttnParams prm) {
   q0 = uniform(q0);
   L = uniform(L);
   const int ngrp = (L * G + kSub - 1) / kSub;
-  if (cb * kWaves >= ngrp) return;  // the whole workgroup: no barrier follows
+  // column groups per wave (kGW) and per workgroup (kGB)
+  constexpr int kGW = GW;
+  constexpr int kGB = kWaves * kGW;
+  if (cb * kGB >= ngrp) return;  // the whole workgroup: no barrier follows
 
   SeqCols sc;
   sc.n = n;
   sc.L = L;
   sc.q0 = q0;
   sc.ngrp = ngrp;
-  const int cg = cb * kWaves + w;
-  uint4 qb[N];
-  load_query_cols<N, true>(qb, prm.q, sc, h, cg, G, Hq, lane);
+  const int cg0 = cb * kGB + w * kGW;  // this wave's first group
+  uint4 qb[kGW][N];
+#pragma unroll
+  for (int g = 0; g < kGW; ++g) load_query_cols<N, true>(qb[g], prm.q, sc, h, cg0 + g, G, Hq, lane);
   // 16-bit types: the core takes a non-negative logit scale; a negative one
   // becomes a negated query (a sign flip, exact)
   const bool neg_scale = prm.scale_log2 < 0.f;
   if constexpr (DT != DT_F32)
     if (neg_scale)
 #pragma unroll
-      for (int kk = 0; kk < N; ++kk) {
-        qb[kk].x ^= 0x80008000u;
-        qb[kk].y ^= 0x80008000u;
-        qb[kk].z ^= 0x80008000u;
-        qb[kk].w ^= 0x80008000u;
-      }
-  const int col = cg * kSub + (lane & 15);
-  const int vis = col < L * G ? n - L + col / G + 1 : 0;  // tokens this lane's column sees
-  // tokens the last column of this wave's group / of the block's last group sees
+      for (int g = 0; g < kGW; ++g)
+#pragma unroll
+        for (int kk = 0; kk < N; ++kk) {
+          qb[g][kk].x ^= 0x80008000u;
+          qb[g][kk].y ^= 0x80008000u;
+          qb[g][kk].z ^= 0x80008000u;
+          qb[g][kk].w ^= 0x80008000u;
+        }
+  // per group: tokens this lane's column sees, and tokens every real column
+  // of the group sees (its first column's); 0 for a group past the last
+  int vis[kGW], vis_first[kGW];
+#pragma unroll
+  for (int g = 0; g < kGW; ++g) {
+    const int col = (cg0 + g) * kSub + (lane & 15);
+    vis[g] = col < L * G ? n - L + col / G + 1 : 0;
+    vis_first[g] = cg0 + g < ngrp ? n - L + ((cg0 + g) * kSub) / G + 1 : 0;
+  }
+  // tokens the last column of this wave's groups / of the block's last group sees
   auto group_limit = [&](int g) {
     int i_last = (g * kSub + kSub - 1) / G;
     i_last = i_last < L - 1 ? i_last : L - 1;
     return n - L + i_last + 1;
   };
-  const int nsub_w = cg < ngrp ? (group_limit(cg) + kSub - 1) / kSub : 0;
-  const int cg_last = (cb + 1) * kWaves < ngrp ? (cb + 1) * kWaves - 1 : ngrp - 1;
+  const int cg_w = cg0 + kGW - 1 < ngrp ? cg0 + kGW - 1 : ngrp - 1;
+  const int nsub_w = cg0 < ngrp ? (group_limit(cg_w) + kSub - 1) / kSub : 0;
+  const int cg_last = (cb + 1) * kGB < ngrp ? (cb + 1) * kGB - 1 : ngrp - 1;
   const int rows_b = group_limit(cg_last);
   const int nsub_b = (rows_b + kSub - 1) / kSub;
   const int nstage_all = (nsub_b + kWaves - 1) / kWaves;
@@ -1631,8 +1647,9 @@ void attn_prefill_kernel(AttnParams prm) {
     }
   };
 
-  WaveState<kMM> st;
-  st.reset();
+  WaveState<kMM> st[kGW];
+#pragma unroll
+  for (int g = 0; g < kGW; ++g) st[g].reset();
   // fp32 scales its logits directly.  16-bit types take |scale| (see above),
   // and a zero scale as the smallest normal float: every logit c * S is then
   // within 2^-24 of zero for |S| < 2^100, so every weight exp2(c * S - m)
@@ -1662,16 +1679,15 @@ void attn_prefill_kernel(AttnParams prm) {
       vo[qd] = *reinterpret_cast<const u32x4*>(pair + ((2 * qd + 1) * 64 + lane) * 16);
     }
   };
-  auto valid_of = [&](int sub) {
-    const int v = vis - sub * kSub;
+  auto valid_of = [&](int g, int sub) {
+    const int v = vis[g] - sub * kSub;
     return v > kSub ? kSub : v;
   };
-  // tokens every real column of this wave sees (its group's first column)
-  const int vis_first = cg < ngrp ? n - L + (cg * kSub) / G + 1 : 0;
   // QK, softmax and PV over the four sub-tiles of stage sg (LDS buffer b):
-  // two pairs for 16-bit types (a pair whose second sub-tile is past this
-  // wave's limit masks it: every token there is past every column's limit),
-  // four single sub-tiles for fp32.
+  // two pairs for 16-bit types, each pair's K and V operands read once and
+  // used by both of the wave's groups (a pair whose second sub-tile is past
+  // a group's limit masks it: every token there is past every column's
+  // limit), four single sub-tiles for fp32.
   auto compute_stage = [&](int sg, int b) {
     if constexpr (DT != DT_F32) {
 #pragma unroll
@@ -1683,9 +1699,12 @@ void attn_prefill_kernel(AttnParams prm) {
           fetch_k(ka0, b, j);
           fetch_k(ka1, b, j + 1);
           fetch_v_pair(ve, vo, b, j / 2);
-          const bool mask = (sub + 2) * kSub > vis_first;
-          attend_pair<DT, N, kMM>(ka0, ka1, ve, vo, qb, mask, valid_of(sub), valid_of(sub + 1),
-                                  scale_log2, r, st);
+#pragma unroll
+          for (int g = 0; g < kGW; ++g) {
+            const bool mask = (sub + 2) * kSub > vis_first[g];
+            attend_pair<DT, N, kMM>(ka0, ka1, ve, vo, qb[g], mask, valid_of(g, sub),
+                                    valid_of(g, sub + 1), scale_log2, r, st[g]);
+          }
         }
       }
     } else {
@@ -1705,7 +1724,7 @@ void attn_prefill_kernel(AttnParams prm) {
             vv[2][qd] = va[qd].z;
             vv[3][qd] = va[qd].w;
           }
-          attend_core<DT, N, kMM>(ka, vv, qb, valid_of(sub), scale_log2, r, st);
+          attend_core<DT, N, kMM>(ka, vv, qb[0], valid_of(0, sub), scale_log2, r, st[0]);
         }
       }
     }
@@ -1728,11 +1747,14 @@ void attn_prefill_kernel(AttnParams prm) {
   }
 
 
-  if (cg < ngrp) {
-    float l = st.l + __shfl_xor(st.l, 16);
+#pragma unroll
+  for (int g = 0; g < kGW; ++g) {
+    if (cg0 + g >= ngrp) break;
+    float l = st[g].l + __shfl_xor(st[g].l, 16);
     l += __shfl_xor(l, 32);
     float o[D / 4];
-    lane_run<D, kMM>(o, st);
+    lane_run<D, kMM>(o, st[g]);
+    const int col = (cg0 + g) * kSub + (lane & 15);
     if (col < L * G) {
       const size_t orow = (size_t)(q0 + col / G) * Hq + (size_t)h * G + col % G;
       if (P == 1) {
@@ -1744,7 +1766,7 @@ void attn_prefill_kernel(AttnParams prm) {
         // part state: unnormalised o, running max (log2 units), normaliser
         const size_t slot = orow * P + part;
         store_run<DT_F32, D>(prm.part_o + slot * D + r * (D / 4), o);
-        if (r == 0) *reinterpret_cast<float2*>(prm.part_ml + slot * 2) = make_float2(st.m, l);
+        if (r == 0) *reinterpret_cast<float2*>(prm.part_ml + slot * 2) = make_float2(st[g].m, l);
       }
     }
   }
@@ -1777,10 +1799,11 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_merge_kernel(AttnParams
   L = L < n ? L : n;
   L = L < prm.max_query_len ? L : prm.max_query_len;
   if (i >= L) return;
+  const int kGB = kWaves * prm.prefill_wave_groups;  // groups per column block
   const int c = i * G + hq % G;  // the column, in its kv head's block
-  const int cb = c / (kWaves * kSub);
+  const int cb = c / (kGB * kSub);
   const int ngrp = (L * G + kSub - 1) / kSub;
-  const int cg_last = (cb + 1) * kWaves < ngrp ? (cb + 1) * kWaves - 1 : ngrp - 1;
+  const int cg_last = (cb + 1) * kGB < ngrp ? (cb + 1) * kGB - 1 : ngrp - 1;
   int i_last = (cg_last * kSub + kSub - 1) / G;
   i_last = i_last < L - 1 ? i_last : L - 1;
   const int rows_b = n - L + i_last + 1;
@@ -1821,9 +1844,13 @@ hipError_t launch_typed(const AttnParams& prm, hipStream_t stream) {
     if (!prm.query_start || prm.num_seqs > 65535 || prm.num_kv_heads > 65535 ||
         prm.prefill_parts < 1 || nx > 0x7fffffffLL)
       return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_prefill_kernel<DT, D, BS>),
-                       dim3((unsigned)nx, (unsigned)prm.num_kv_heads, (unsigned)prm.num_seqs),
-                       block, 0, stream, prm);
+    const dim3 grid((unsigned)nx, (unsigned)prm.num_kv_heads, (unsigned)prm.num_seqs);
+    if (prm.prefill_wave_groups == 1)
+      hipLaunchKernelGGL((attn_prefill_kernel<DT, D, BS, 1>), grid, block, 0, stream, prm);
+    else if constexpr (DT != DT_F32)
+      hipLaunchKernelGGL((attn_prefill_kernel<DT, D, BS, 2>), grid, block, 0, stream, prm);
+    else
+      return hipErrorInvalidValue;
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || prm.prefill_parts == 1) return err;
     const long long waves = (long long)prm.num_seqs * prm.max_query_len * prm.num_q_heads;
@@ -1923,6 +1950,19 @@ int32_t prefill_parts_for(int32_t num_seqs, int32_t num_kv_heads, int32_t prefil
   if (p > by_len) p = by_len;
   if (p > kPrefillMaxParts) p = kPrefillMaxParts;
   return p < 1 ? 1 : (int32_t)p;
+}
+
+PrefillPlan prefill_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_groups,
+                         int32_t max_context_len, int dtype) {
+  auto blocks_of = [&](int32_t gw) { return (max_groups + kWaves * gw - 1) / (kWaves * gw); };
+  PrefillPlan pl{1, blocks_of(1), 1};
+  if (dtype != DT_F32) {
+    const long long wgs2 = (long long)num_seqs * num_kv_heads * blocks_of(2);
+    if (wgs2 < kPrefillMinWorkgroups || wgs2 >= 2LL * kPrefillMinWorkgroups)
+      pl = PrefillPlan{2, blocks_of(2), 1};
+  }
+  pl.parts = prefill_parts_for(num_seqs, num_kv_heads, pl.blocks, max_context_len);
+  return pl;
 }
 
 AttnWorkspace prefill_workspace_layout(int32_t num_query_tokens, int32_t num_q_heads,

@@ -28,13 +28,18 @@ constexpr int kMaxMultiSeqs = 2048;       // batch limit with several new tokens
 // Multi-token calls with at least this many columns (max_query_len * G) per
 // sequence take the prefill path.
 constexpr int kPrefillMinCols = 64;
+// Column groups of 16 per wave on the prefill path: two (16-bit types only;
+// each K/V operand a wave reads from LDS serves both, two workgroups per
+// compute unit) or one (three workgroups per compute unit).  A workgroup
+// (column block) takes kStreamWaves times as many.
 // Up to this many sequences the prefill path dispatches them longest context
 // first (each workgroup ranks the context lengths itself).
 constexpr int kPrefillRankSeqs = 256;
 // The prefill path splits contexts when a call has fewer than this many
 // (sequence, kv head, column block) workgroups, into at most kPrefillMaxParts
-// parts of at least kPrefillMinPartTokens tokens.
-constexpr int kPrefillMinWorkgroups = 1024;
+// parts of at least kPrefillMinPartTokens tokens.  (512: one workgroup per
+// slot of the chip at two per compute unit.)
+constexpr int kPrefillMinWorkgroups = 512;
 constexpr int kPrefillMaxParts = 16;
 constexpr int kPrefillMinPartTokens = 512;
 // Positions (H_kv x sub-tiles of the batch) the stream path indexes in 32 bits;
@@ -87,6 +92,8 @@ struct AttnParams {
   // than one, part states go to part_o [rows * H_q * parts, D] and part_ml
   // [rows * H_q * parts, 2] (row = query row) and a merge writes `out`.
   int32_t prefill_parts;
+  // Prefill path: column groups per wave (1 or 2; see prefill_plan).
+  int32_t prefill_wave_groups;
 };
 
 // Workspace layout of one decode call, shared by the size query and the call.
@@ -100,6 +107,17 @@ AttnWorkspace attn_workspace_layout(int32_t num_seqs, int32_t slot_cols, int32_t
 // workspace of the part states (0 bytes with one part).
 int32_t prefill_parts_for(int32_t num_seqs, int32_t num_kv_heads, int32_t prefill_blocks,
                           int32_t max_context_len);
+// Launch plan of a prefill-path call (max_groups 16-column groups per
+// sequence and kv head; dtype 0 f32, 1 f16, 2 bf16): column groups per wave,
+// column blocks (workgroups) per (sequence, kv head) and context parts.  Two
+// groups per wave where the call is cut into equal parts or has at least two
+// workgroups per slot of the chip; otherwise one, whose twice as many
+// smaller workgroups balance unequal contexts better.
+struct PrefillPlan {
+  int32_t wave_groups, blocks, parts;
+};
+PrefillPlan prefill_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_groups,
+                         int32_t max_context_len, int dtype);
 AttnWorkspace prefill_workspace_layout(int32_t num_query_tokens, int32_t num_q_heads,
                                        int32_t head_dim, int32_t parts);
 

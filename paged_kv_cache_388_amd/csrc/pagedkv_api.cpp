@@ -223,9 +223,8 @@ size_t attention_workspace(const pkv_pool& pool, int32_t num_seqs, int32_t num_q
   const int32_t group = num_q_heads / pool.num_kv_heads;
   const int32_t groups = max_groups_for(max_query_len, group);
   if (multi && prefill_route(max_query_len, group)) {
-    const int32_t blocks = (groups + pkv::kStreamWaves - 1) / pkv::kStreamWaves;
     const int32_t parts =
-        pkv::prefill_parts_for(num_seqs, pool.num_kv_heads, blocks, max_context_len);
+        pkv::prefill_plan(num_seqs, pool.num_kv_heads, groups, max_context_len, pool.dtype).parts;
     // every query row may belong to a split context: bound by the rows the
     // batch can hold (num_seqs * max_query_len)
     const long long rows = (long long)num_seqs * max_query_len;
@@ -285,9 +284,11 @@ pkv_status attention_call(const char* what, void* out, const void* q, const void
                 "(kv heads x 16-column groups x 16-token sub-tiles)",
                 pkv::kMaxMultiSeqs);
   const int32_t cols = slot_cols_for(max_query_len, group);
-  const int32_t pf_blocks = prefill ? (groups + pkv::kStreamWaves - 1) / pkv::kStreamWaves : 0;
-  const int32_t pf_parts =
-      prefill ? pkv::prefill_parts_for(num_seqs, pool.num_kv_heads, pf_blocks, max_context_len) : 1;
+  const pkv::PrefillPlan plan =
+      prefill ? pkv::prefill_plan(num_seqs, pool.num_kv_heads, groups, max_context_len, pool.dtype)
+              : pkv::PrefillPlan{1, 0, 1};
+  const int32_t pf_blocks = plan.blocks;
+  const int32_t pf_parts = plan.parts;
   const pkv::AttnWorkspace lay =
       prefill ? pkv::prefill_workspace_layout(num_query_tokens, num_q_heads, pool.head_dim, pf_parts)
               : pkv::attn_workspace_layout(num_seqs, cols, num_q_heads, pool.head_dim,
@@ -357,6 +358,7 @@ pkv_status attention_call(const char* what, void* out, const void* q, const void
   prm.slot_cols = cols;
   prm.prefill_blocks = pf_blocks;
   prm.prefill_parts = pf_parts;
+  prm.prefill_wave_groups = plan.wave_groups;
   hipError_t err = pkv::launch_paged_attention(prm, pool.dtype, pool.head_dim, pool.block_size, stream);
   return err == hipSuccess ? PKV_OK : hip_fail(err, what);
 }

@@ -69,6 +69,24 @@ def test_scale_negative_zero_and_large(path, dtype, mult):
     _run(w, f"{path} {dtype} scale {mult}/sqrt(D)")
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64)])
+@pytest.mark.parametrize("plan", ["one_group_per_wave", "two_groups_per_wave"])
+def test_prefill_path_wave_group_plans(dtype, D, plan):
+    """The prefill path runs one or two 16-column groups per wave by the
+    call's workgroup count: 64 sequences x 8 kv heads with 32 new tokens at
+    G = 4 (8 groups, one 8-group block each) give 512 two-group workgroups,
+    which takes one group per wave; 128 sequences give 1024, which takes two.
+    Ragged new-token counts and contexts, NaN-poisoned pools."""
+    B = 64 if plan == "one_group_per_wave" else 128
+    rng = np.random.default_rng(61)
+    ctx = rng.integers(32, 200, size=B).tolist()
+    qlens = [32] + rng.integers(1, 33, size=B - 1).tolist()
+    w = wl.build(f"pf_plan_{plan}_{dtype}", 61, rng, ctx, 32, 8, D, 16, dtype, poison=True,
+                 query_lens=qlens)
+    assert w.max_query_len * 4 >= 64
+    _run(w, f"prefill path, {plan}, {dtype} D{D}")
+
+
 def test_whole_context_chunks():
     rng = np.random.default_rng(43)
     ctx = [1, 16, 33, 64]
