@@ -224,6 +224,20 @@ __device__ __forceinline__ void restage_k(uint4 (&a)[N], const Tile<N>& t, char*
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Maximum of x over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four row groups
+// of one MFMA column): two row swaps (v_permlane16_swap, v_permlane32_swap),
+// each one VALU instruction with no LDS round trip.  The NaN-propagating
+// maximum needs no quieting of its inputs (fmaxf's NaN rules make the
+// compiler add one instruction per operand); logits are finite here.
+__device__ __forceinline__ float rows_max(float x) {
+  unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  u = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // QK, mask, online softmax and PV of one 16-token sub-tile whose K is in the
 // MFMA A operand order (ka) and V in its load order (vv); `valid` tokens
 // (from the sub-tile's first) are real for this lane's column, the rest are
@@ -258,10 +272,9 @@ __device__ __forceinline__ void attend_core(const uint4 (&ka)[N], const uint32_t
   float sv[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) sv[e] = (4 * r + e < valid) ? S[e] * scale_log2 : kNegInf;
-  float mloc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-  const float m_new = fmaxf(st.m, mloc);
+  const auto mx = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+  const float mloc = rows_max(mx(mx(sv[0], sv[1]), mx(sv[2], sv[3])));
+  const float m_new = mx(st.m, mloc);
   const float mb = m_new == kNegInf ? 0.f : m_new;
   const float alpha = fast_exp2(st.m - mb);
   float pe[4];
@@ -353,20 +366,6 @@ __device__ __forceinline__ void attend_core(const uint4 (&ka)[N], const uint32_t
 // stream and the accumulators stay in their registers (a separate copy of
 // the pair per case made the compiler move all of them at every join).
 constexpr float kLazyLog2 = 8.f;
-
-// Maximum of x over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four row groups
-// of one MFMA column): two row swaps (v_permlane16_swap, v_permlane32_swap),
-// each one VALU instruction with no LDS round trip.  The NaN-propagating
-// maximum needs no quieting of its inputs (fmaxf's NaN rules make the
-// compiler add one instruction per operand); logits are finite here.
-__device__ __forceinline__ float rows_max(float x) {
-  unsigned u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  u = __float_as_uint(x);
-  const auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
 
 template <int DT, int N, int kMM>
 __device__ __forceinline__ void attend_pair(const uint4 (&ka0)[N], const uint4 (&ka1)[N],
