@@ -87,6 +87,29 @@ def test_prefill_path_wave_group_plans(dtype, D, plan):
     _run(w, f"prefill path, {plan}, {dtype} D{D}")
 
 
+@pytest.mark.parametrize("G", [3, 5])
+@pytest.mark.parametrize("batch", ["64_sequences", "3_sequences_split"])
+def test_prefill_path_groups_straddling_tokens(G, batch):
+    """Query-head groups that do not divide 16: a 16-column group straddles
+    new tokens and a column block ends inside one.  64 sequences x 8 kv heads
+    with 32 new tokens give 512 two-group workgroups at G = 3 (one group per
+    wave, 4-group blocks) and 1024 at G = 5 (two groups per wave, 8-group
+    blocks); 3 sequences x 2 kv heads with up to 100 new tokens give 18 or 24
+    (two groups per wave, contexts cut into two parts and merged)."""
+    rng = np.random.default_rng(62)
+    if batch == "64_sequences":
+        B, Hkv = 64, 8
+        ctx = rng.integers(40, 300, size=B).tolist()
+        qlens = [32] + rng.integers(1, 33, size=B - 1).tolist()
+    else:
+        B, Hkv = 3, 2
+        ctx, qlens = [700, 90, 1500], [64, 30, 100]
+    w = wl.build(f"pf_G{G}_{batch}", 62, rng, ctx, G * Hkv, Hkv, 128, 16, "bf16", poison=True,
+                 query_lens=qlens)
+    assert w.max_query_len * G >= 64
+    _run(w, f"prefill path G={G}, {batch}")
+
+
 def test_whole_context_chunks():
     rng = np.random.default_rng(43)
     ctx = [1, 16, 33, 64]
