@@ -367,13 +367,16 @@ __device__ __forceinline__ void attend_core(const uint4 (&ka)[N], const uint32_t
 // the pair per case made the compiler move all of them at every join).
 constexpr float kLazyLog2 = 8.f;
 
-template <int DT, int N, int kMM>
-__device__ __forceinline__ void attend_pair(const uint4 (&ka0)[N], const uint4 (&ka1)[N],
-                                            const u32x4 (&ve)[N], const u32x4 (&vo)[N],
-                                            const uint4 (&qb)[N], bool mask, int valid0, int valid1,
-                                            float scale_log2, int r, WaveState<kMM>& st) {
+// QK of a sub-tile pair: two independent MFMA chains.  Issued ahead of the
+// softmax of an earlier product, the MFMAs run while the VALU works on it
+// (the softmax's rescale branch would otherwise end the scheduling region
+// between them).
+template <int DT, int N>
+__device__ __forceinline__ void qk_pair(const uint4 (&ka0)[N], const uint4 (&ka1)[N],
+                                        const uint4 (&qb)[N], floatx4& S0, floatx4& S1) {
   static_assert(DT != DT_F32, "16-bit types only");
-  floatx4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+  S0 = floatx4{0.f, 0.f, 0.f, 0.f};
+  S1 = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < N; ++kk) {
     if constexpr (DT == DT_F16) {
@@ -388,6 +391,15 @@ __device__ __forceinline__ void attend_pair(const uint4 (&ka0)[N], const uint4 (
                                                    __builtin_bit_cast(bf16x8, qb[kk]), S1, 0, 0, 0);
     }
   }
+}
+
+// Online softmax and PV of a sub-tile pair whose scores qk_pair produced.
+template <int DT, int N, int kMM>
+__device__ __forceinline__ void softmax_pv_pair(const floatx4& S0, const floatx4& S1,
+                                                const u32x4 (&ve)[N], const u32x4 (&vo)[N],
+                                                bool mask, int valid0, int valid1,
+                                                float scale_log2, int r, WaveState<kMM>& st) {
+  static_assert(DT != DT_F32, "16-bit types only");
   // Raw scores S; the logit is c * S with c = scale_log2 > 0 (a negative
   // scale arrives as a negated query, a zero one as the smallest normal
   // float).  Multiplying by c > 0 is monotone in floating point, so the
@@ -1697,12 +1709,16 @@ void attn_prefill_kernel(AttnParams prm) {
           u32x4 ve[N], vo[N];
           fetch_k(ka0, b, j);
           fetch_k(ka1, b, j + 1);
+          // every group's QK first, then each group's softmax and PV
+          floatx4 S[kGW][2];
+#pragma unroll
+          for (int g = 0; g < kGW; ++g) qk_pair<DT, N>(ka0, ka1, qb[g], S[g][0], S[g][1]);
           fetch_v_pair(ve, vo, b, j / 2);
 #pragma unroll
           for (int g = 0; g < kGW; ++g) {
             const bool mask = (sub + 2) * kSub > vis_first[g];
-            attend_pair<DT, N, kMM>(ka0, ka1, ve, vo, qb[g], mask, valid_of(g, sub),
-                                    valid_of(g, sub + 1), scale_log2, r, st[g]);
+            softmax_pv_pair<DT, N, kMM>(S[g][0], S[g][1], ve, vo, mask, valid_of(g, sub),
+                                        valid_of(g, sub + 1), scale_log2, r, st[g]);
           }
         }
       }
