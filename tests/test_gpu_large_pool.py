@@ -1,0 +1,134 @@
+"""Pools far beyond 4 GiB (needs an MI355X).
+
+A pool on an MI355X may hold hundreds of GiB, so a tile's byte offset
+(block id x heads x tile bytes) does not fit 32 bits.  Each case runs one
+step twice: once on a compact pool, and once with the same blocks placed at
+the top of a pool of about 20 GiB per cache, whose other blocks hold NaN.
+The block tables, slots and copy pairs of the second run are shifted by the
+same block offset.  Placement does not change the result (the block table is
+the only map from logical to physical blocks), so outputs and the live
+blocks must match bit for bit; the compact run is also checked against the
+oracle.  An offset truncated to 32 bits would read NaN blocks or write
+outside the live region.
+"""
+
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_388_amd import _lib
+from paged_kv_cache_388_amd import workloads as wl
+
+from gpu_common import (DeviceWorkload, TORCH_DT, check_attention, oracle_pools_after_step,
+                        oracle_step, to_host)
+
+pytestmark = pytest.mark.gpu
+
+POOL_BYTES = 20 << 30       # per cache, so live tiles start above 16 GiB
+
+
+def _nan_pool(nb, like):
+    """A pool of nb blocks shaped like ``like``, every element NaN."""
+    return torch.full((nb,) + tuple(like.shape[1:]), float("nan"), dtype=like.dtype,
+                      device=like.device)
+
+
+def _shift(ids, off):
+    """Block ids (or slots, with off pre-multiplied) shifted by off; negative
+    entries (unused table entries, skipped slots) stay as they are."""
+    return torch.where(ids >= 0, ids + off, ids)
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+
+def _far_copy(dw):
+    """The device workload dw with its pools moved to the top of ~20 GiB pools."""
+    block_bytes = dw.k_cache[0].numel() * dw.k_cache.element_size()
+    nb_small = dw.k_cache.shape[0]
+    nb_big = POOL_BYTES // block_bytes
+    off = nb_big - nb_small
+    assert off * block_bytes >= (16 << 30)
+    far = copy.copy(dw)
+    far.k_cache = _nan_pool(nb_big, dw.k_cache)
+    far.v_cache = _nan_pool(nb_big, dw.v_cache)
+    far.k_cache[off:].copy_(dw.k_cache)
+    far.v_cache[off:].copy_(dw.v_cache)
+    far.block_tables = _shift(dw.block_tables, off)
+    far.slot_mapping = _shift(dw.slot_mapping, off * dw.w.block_size)
+    far.block_mapping = _shift(dw.block_mapping, off)
+    far.out = torch.empty_like(dw.out)
+    far.workspace = torch.zeros_like(dw.workspace)
+    return far, off
+
+
+def _check_pools(far, near, off):
+    for big, small in ((far.k_cache, near.k_cache), (far.v_cache, near.v_cache)):
+        assert torch.equal(_bits(big[off:]), _bits(small)), "live blocks differ"
+        # the blocks just below the live region were never written
+        assert torch.isnan(big[off - 64:off].float()).all()
+
+
+def _case(kind, dtype, D, bs, G):
+    rng = np.random.default_rng(388100 + D + bs + G)
+    ctx = [1, 17, 100, 513, 1300, 3000]
+    qlens = {"decode": None, "multi_stream": [1, 3, 3, 2, 5, 1], "prefill": [1, 17, 64, 64, 64, 64]}
+    w = wl.build(f"far_{kind}", 388100, rng, ctx, G * 4, 4, D, bs, dtype, poison=True,
+                 query_lens=qlens[kind])
+    # copy-on-write pairs: live blocks into the free blocks no table references
+    live = set(int(b) for b in w.block_tables[w.block_tables >= 0])
+    free = [b for b in range(w.k_cache.shape[0]) if b not in live]
+    pairs = np.stack([np.array(sorted(live)[:len(free)][:6]), np.array(free[:6])], axis=1)
+    w.block_mapping = pairs.astype(np.int32)
+    return w
+
+
+@pytest.mark.parametrize("kind,dtype,D,bs,G", [
+    ("decode", "bf16", 128, 16, 4),
+    ("decode", "f16", 64, 32, 1),
+    ("multi_stream", "bf16", 128, 16, 4),
+    ("prefill", "bf16", 128, 16, 4),
+    ("prefill", "f16", 64, 32, 4),
+])
+def test_pool_above_16_gib(kind, dtype, D, bs, G):
+    w = _case(kind, dtype, D, bs, G)
+    print(f"[gpu] far pool {kind} {dtype} D={D} bs={bs} G={G}", flush=True)
+    near = DeviceWorkload(w)
+    far, off = _far_copy(near)
+    got_near = near.step()
+    got_far = far.step()
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(got_far), _bits(got_near)), "output depends on block placement"
+    _check_pools(far, near, off)
+    kc, vc = oracle_pools_after_step(w)
+    assert np.array_equal(to_host(near.k_cache, dtype).view(np.uint8), kc.view(np.uint8))
+    assert np.array_equal(to_host(near.v_cache, dtype).view(np.uint8), vc.view(np.uint8))
+    check_attention(to_host(got_near, dtype), oracle_step(w, pools=(kc, vc)), dtype,
+                    f"far pool {kind}")
+    del far
+    torch.cuda.empty_cache()
+
+
+def test_swap_blocks_above_16_gib():
+    w = _case("decode", "bf16", 128, 16, 4)
+    print("[gpu] far pool swap bf16 D=128 bs=16", flush=True)
+    near = DeviceWorkload(w)
+    far, off = _far_copy(near)
+    rng = np.random.default_rng(388101)
+    ids = rng.permutation(near.k_cache.shape[0])[:40].astype(np.int32)
+    ids_dev = torch.from_numpy(ids).cuda()
+    img_near = _lib.paged_swap_out(near.k_cache, near.v_cache, ids_dev)
+    img_far = _lib.paged_swap_out(far.k_cache, far.v_cache, ids_dev + off)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(img_far), _bits(img_near))
+    # back in, reversed, over the same live blocks of both pools
+    back = torch.flip(ids_dev, (0,))
+    _lib.paged_swap_in(img_near, near.k_cache, near.v_cache, back)
+    _lib.paged_swap_in(img_far, far.k_cache, far.v_cache, back + off)
+    torch.cuda.synchronize()
+    _check_pools(far, near, off)
+    del far
+    torch.cuda.empty_cache()
