@@ -42,6 +42,8 @@ if not _CPU_WORKER:
     from paged_kv_cache_388_amd import workloads as wl  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
+# the CPU baseline runs at most this many oracle processes, whatever the host
+CPU_PROCESS_CAP = 16
 # dense MFMA peaks of MI355X, TFLOP/s, by the dtype the products run in
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 PREFILL_MIN_COLS = 64      # max_query_len * G at which a multi call takes the prefill path
@@ -88,12 +90,13 @@ def attention_flops(w):
     return 4 * w.head_dim * G * w.num_kv_heads * visible
 
 
-def counter_traffic(workload):
-    """HBM bytes per decode call from the committed counter summary of this
-    workload, or None if there is none or the kernel source has changed since
-    the counters were taken (the summary records the source's SHA-256)."""
+def counter_traffic(workload, kernel="attn_stream_kernel"):
+    """HBM bytes per attention call from the committed counter summary of this
+    kernel and workload, or None if there is none or the kernel source has
+    changed since the counters were taken (the summary records the source's
+    SHA-256)."""
     import hashlib
-    path = os.path.join(PROFILES, f"attn_stream_kernel_{workload}_hbm_counters.md")
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -107,6 +110,18 @@ def counter_traffic(workload):
     if fields.get("source_sha256") != sha or "traffic_bytes_per_call" not in fields:
         return None
     return int(fields["traffic_bytes_per_call"])
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where absent)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def _oracle_pass(A, seq_list, seconds):
@@ -247,6 +262,8 @@ def cpu_baseline(w, min_seconds, workers):
             shm.close()
             shm.unlink()
     return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
+            "usable_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "process_cap": CPU_PROCESS_CAP,
             "sample": (f"{rows} query rows of {seqs} sequence-attentions of this step "
                        f"({seqs / w.num_seqs:.2f} passes over the {w.num_seqs}-sequence batch, "
                        f"the last one possibly in part) after its cache writes "
@@ -492,6 +509,35 @@ def read_probe(mib, steps, warmup):
                       "read_GBps": round(n / (ms * 1e-3) / 1e9, 1)}))
 
 
+def reread_probe(mib, rounds, steps, warmup):
+    """Time the library's re-read probe: a buffer of `mib` MiB read `rounds`
+    times per call, each XCD re-reading only its own eighth.  Up to 8 L2s
+    (32 MiB) the re-reads come from the XCDs' L2s, above that from the
+    Infinity Cache: the cache-side read ceilings that a decode over blocks
+    shared between sequences runs against."""
+    import torch
+    from paged_kv_cache_388_amd import _lib
+    _lib.load()
+    n = int(mib * (1 << 20)) // 16 * 16
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.random_(0, 255)
+    sink = torch.zeros(_lib.STREAM_READ_WORKGROUPS, dtype=torch.int32, device="cuda")
+    for _ in range(warmup):
+        _lib.pkv_stream_reread(src, rounds, sink)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        a[i].record(stream)
+        _lib.pkv_stream_reread(src, rounds, sink)
+        b[i].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([x.elapsed_time(y) for x, y in zip(a, b)]))
+    print(json.dumps({"reread_probe_bytes": n, "rounds": rounds, "ms_per_call": round(ms, 4),
+                      "read_GBps": round(n * rounds / (ms * 1e-3) / 1e9, 1)}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -508,13 +554,22 @@ def main():
                     help="duration of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--cpu-workers", type=int, default=0,
                     help="processes of the CPU oracle baseline (default: the usable cores, "
-                         "at most 16)")
+                         f"at most {CPU_PROCESS_CAP})")
     ap.add_argument("--read-probe-mib", type=int, default=0,
                     help="instead of the decode step, time pkv_stream_read of this many MiB "
                          "(the achievable read-bandwidth reference)")
+    ap.add_argument("--reread-probe-mib", type=float, default=0,
+                    help="instead of the decode step, time pkv_stream_reread of this many MiB "
+                         "(the L2 / Infinity Cache read ceiling; see --reread-rounds)")
+    ap.add_argument("--reread-rounds", type=int, default=64,
+                    help="times the re-read probe reads its buffer per call")
     ap.add_argument("--cold", action="store_true",
                     help="write a 1 GiB scrub buffer before every timed step, so that no "
                          "K/V byte is served from L2 or the Infinity Cache")
+    ap.add_argument("--decode-path", choices=("stream", "grid"), default="stream",
+                    help="grid: every decode call takes the 512-token partition path (one "
+                         "workgroup per (kv head, sequence, partition) and the partition "
+                         "merge; PAGEDKV_DECODE_PATH=grid) instead of the stream path")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step as one captured HIP graph (the attention call's "
                          "events are then taken in a loop of their own)")
@@ -547,7 +602,12 @@ def main():
     if args.read_probe_mib > 0:
         read_probe(args.read_probe_mib, args.steps, args.warmup)
         return
+    if args.reread_probe_mib > 0:
+        reread_probe(args.reread_probe_mib, args.reread_rounds, args.steps, args.warmup)
+        return
 
+    if args.decode_path == "grid":
+        os.environ["PAGEDKV_DECODE_PATH"] = "grid"   # read by the library on every call
     t_gen = time.perf_counter()
     w = wl.named(args.workload)
     print(f"[bench] workload {w.name} generated in {time.perf_counter() - t_gen:.1f} s",
@@ -555,7 +615,7 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
+        workers = args.cpu_workers or min(CPU_PROCESS_CAP, len(os.sched_getaffinity(0)))
         cpu = cpu_baseline(w, args.cpu_seconds, workers)
         print(f"[bench] cpu oracle: {cpu['sample']}", file=sys.stderr, flush=True)
 
@@ -716,11 +776,13 @@ def main():
                     "algorithmic_bytes_per_launch": alg,
                     "hbm_GBps_of_algorithmic_bytes": round(achieved, 1)}
     else:
+        grid = args.decode_path == "grid" and not w.multi
+        kname = "attn_grid_kernel" if grid else "attn_stream_kernel"
+        merge = "attn_reduce_kernel" if grid else "attn_stream_merge_kernel"
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                    "traffic": counter_traffic(w.name),
-                    "kernel": (f"attn_stream_kernel<{w.dtype},{w.head_dim},{w.block_size}> + "
-                               "attn_stream_merge_kernel (one "
+                    "traffic": counter_traffic(w.name, kname),
+                    "kernel": (f"{kname}<{w.dtype},{w.head_dim},{w.block_size}> + {merge} (one "
                                f"{'paged_attention_multi' if w.multi else 'paged_attention_decode'}"
                                " call)"),
                     "algorithmic_bytes_per_launch": alg,
@@ -752,7 +814,8 @@ def main():
                             + ("paged_attention_multi" if w.multi else "paged_attention_decode")),
                    "new_tokens": int(w.q.shape[0]),
                    "parallelism": "single GPU", "cold": bool(args.cold),
-                   "graph": bool(args.graph)},
+                   "graph": bool(args.graph),
+                   **({"decode_path": args.decode_path} if not w.multi else {})},
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "seqs_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "new_tokens_per_s": round(w.q.shape[0] / (ms_per_step * 1e-3), 1),

@@ -114,10 +114,21 @@ PKV_API pkv_status paged_kv_append(const void* key, const void* value,
  * Bytes of workspace paged_attention_decode needs for this shape on the
  * current device (the kernel's grid follows the device's compute-unit count):
  * per-sequence sub-tile offsets and fp32 partial softmax states of the
- * sequences whose context is split between waves.  Independent of the context
- * lengths for batches up to 4096 sequences; above that it grows with
- * ceil(max_context_len / 512).  Returns 0 for invalid input (including
- * num_q_heads not a multiple of pool.num_kv_heads).
+ * sequences whose context is split between waves.  Query it on the device
+ * the call will run on.  Up to 4096 sequences (the stream path) the size is
+ * independent of the context lengths, and non-zero even for short contexts:
+ * every workgroup has two partial-state slots and every wave a parking row,
+ * (2 * workgroups + waves) * min(16, G) rows of head_dim + 2 floats, plus
+ * num_seqs + 1 int32 offsets.  Above 4096 sequences (the grid path) it is
+ * num_seqs * num_q_heads * ceil(max_context_len / 512) * (head_dim + 2)
+ * floats, and 0 when max_context_len <= 512.  Returns 0 for invalid input
+ * (including num_q_heads not a multiple of pool.num_kv_heads).
+ *
+ * Measurement switch: with PAGEDKV_DECODE_PATH=grid in the environment,
+ * every decode call and this query take the grid path (one workgroup per
+ * (kv head, sequence, 512-token partition), then the partition merge)
+ * whatever the batch.  Read on every call; the query and the call must see
+ * the same setting.
  */
 PKV_API size_t paged_attention_workspace_bytes(pkv_pool pool, int32_t num_seqs,
                                                int32_t num_q_heads, int32_t max_context_len);
@@ -310,6 +321,18 @@ PKV_API pkv_status pkv_stream_copy(void* dst, const void* src, size_t bytes,
  */
 PKV_API pkv_status pkv_stream_read(const void* src, size_t bytes, uint32_t* sink,
                                    hipStream_t stream);
+
+/*
+ * pkv_stream_reread — read `bytes` bytes (a multiple of 16) `rounds` times
+ * with the same loads, each XCD re-reading only its own eighth of the buffer
+ * (workgroup b of 2048, on XCD b mod 8, reads range (b + 8 r) mod 2048 of the
+ * buffer in round r).  With a buffer of up to 8 L2s the re-reads are served
+ * by the XCDs' L2s, with a larger one by the Infinity Cache: the cache
+ * ceilings for a decode whose blocks are shared between sequences.  sink as
+ * for pkv_stream_read.  Not part of the attention method.
+ */
+PKV_API pkv_status pkv_stream_reread(const void* src, size_t bytes, int32_t rounds,
+                                     uint32_t* sink, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Host block manager (host memory only; no device work).

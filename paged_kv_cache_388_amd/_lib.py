@@ -68,6 +68,8 @@ def load():
     lib.pkv_stream_copy.restype = c_i32
     lib.pkv_stream_read.argtypes = [c_vp, c_sz, c_vp, c_vp]
     lib.pkv_stream_read.restype = c_i32
+    lib.pkv_stream_reread.argtypes = [c_vp, c_sz, c_i32, c_vp, c_vp]
+    lib.pkv_stream_reread.restype = c_i32
     lib.pkv_status_string.argtypes = [c_i32]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_last_error.argtypes = []
@@ -85,6 +87,16 @@ def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _scratch(nbytes, device, stream):
+    """Uninitialised device bytes for a call that runs on ``stream`` (None:
+    the current stream).  Allocated while that stream is current, so the
+    caching allocator hands the memory to other work only once that stream
+    has passed the call's kernels."""
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    with torch.cuda.stream(s):
+        return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
 def _ptr(t):
@@ -167,7 +179,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         raise ValueError("block_tables / context_lens disagree with q on num_seqs")
     need = paged_attention_workspace_bytes(k_cache, B, Hq, int(max_context_len))
     if workspace is None:
-        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+        workspace = _scratch(need, dev, stream)
     else:
         _need(workspace, "workspace", device=dev)
     _check(load().paged_attention_decode(
@@ -206,7 +218,7 @@ def paged_attention_multi(out, q, k_cache, v_cache, block_tables, context_lens, 
         raise ValueError("block_tables [B, *], context_lens [B], query_start [B + 1] disagree")
     need = paged_attention_multi_workspace_bytes(k_cache, B, Hq, max_query_len, max_context_len)
     if workspace is None:
-        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+        workspace = _scratch(need, dev, stream)
     else:
         _need(workspace, "workspace", device=dev)
     _check(load().paged_attention_multi(
@@ -230,14 +242,14 @@ def paged_copy_blocks(k_cache, v_cache, block_mapping, stream=None):
 SWAP_STAGING_BYTES = 64 << 20
 
 
-def _swap_args(k_cache, v_cache, block_ids, staging):
+def _swap_args(k_cache, v_cache, block_ids, staging, stream):
     pool = _pools(k_cache, v_cache)
     _need(block_ids, "block_ids", dtype=torch.int32, dim=1, device=k_cache.device)
     entry = 2 * k_cache[0].numel() * k_cache.element_size()
     n = block_ids.shape[0]
     if staging is None:
         nbytes = min(max(n, 1) * entry, max(entry, SWAP_STAGING_BYTES // entry * entry))
-        staging = torch.empty(nbytes, dtype=torch.uint8, device=k_cache.device)
+        staging = _scratch(nbytes, k_cache.device, stream)
     else:
         _need(staging, "staging", device=k_cache.device)
     return pool, n, (n, 2) + tuple(k_cache.shape[1:]), staging
@@ -254,7 +266,7 @@ def paged_swap_out(k_cache, v_cache, block_ids, host_image=None, staging=None, s
     """Copy the listed blocks to a host image [n, 2, H_kv, bs, D] (entry i:
     block_ids[i]'s K then V).  Allocates a pinned image when none is given.
     Asynchronous: the image is complete once the stream is synchronized."""
-    pool, n, shape, staging = _swap_args(k_cache, v_cache, block_ids, staging)
+    pool, n, shape, staging = _swap_args(k_cache, v_cache, block_ids, staging, stream)
     if host_image is None:
         host_image = torch.empty(shape, dtype=k_cache.dtype, pin_memory=True)
     _need_host(host_image, "host_image", k_cache.dtype, shape)
@@ -268,7 +280,7 @@ def paged_swap_in(host_image, k_cache, v_cache, block_ids, staging=None, stream=
     """Write entry i of a host image into block block_ids[i] of both pools
     (distinct destinations).  The host image must stay untouched until the
     stream has reached the end of the call."""
-    pool, n, shape, staging = _swap_args(k_cache, v_cache, block_ids, staging)
+    pool, n, shape, staging = _swap_args(k_cache, v_cache, block_ids, staging, stream)
     _need_host(host_image, "host_image", k_cache.dtype, shape)
     _check(load().paged_swap_in(_ptr(host_image), n, _ptr(k_cache), _ptr(v_cache), pool,
                                 _ptr(block_ids), _ptr(staging),
@@ -297,6 +309,18 @@ def pkv_stream_read(src, sink, stream=None):
         raise ValueError("sink must hold 2048 32-bit words")
     _check(load().pkv_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
                                   _stream(stream)))
+
+
+def pkv_stream_reread(src, rounds, sink, stream=None):
+    """Read every byte of src ``rounds`` times, each XCD re-reading only its
+    own eighth of it (the L2 / Infinity Cache read ceilings); sink as for
+    pkv_stream_read."""
+    _need(src, "src")
+    _need(sink, "sink", device=src.device)
+    if sink.numel() * sink.element_size() < 4 * STREAM_READ_WORKGROUPS:
+        raise ValueError("sink must hold 2048 32-bit words")
+    _check(load().pkv_stream_reread(_ptr(src), src.numel() * src.element_size(), int(rounds),
+                                    _ptr(sink), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

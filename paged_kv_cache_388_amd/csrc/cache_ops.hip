@@ -106,17 +106,11 @@ __global__ __launch_bounds__(kThreads) void stream_copy_kernel(uint4* __restrict
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Read-only stream: workgroup b reads the contiguous range
-// [b * per_wg, (b + 1) * per_wg) of 16-byte chunks with nontemporal loads,
-// eight in flight per thread, folds them with XOR and writes one word, so the
-// loads cannot be dropped.
-__global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __restrict__ src,
-                                                               int64_t chunks, int64_t per_wg,
-                                                               uint32_t* __restrict__ sink) {
-  __shared__ uint32_t red[kThreads / 64];
-  const int64_t begin = (int64_t)blockIdx.x * per_wg;
-  const int64_t end = begin + per_wg < chunks ? begin + per_wg : chunks;
-  u32x4 acc = {0u, 0u, 0u, 0u};
+// XOR-fold of the 16-byte chunks [begin, end) of src read by this workgroup
+// with nontemporal loads (the attention kernels' policy), eight in flight per
+// thread.
+__device__ __forceinline__ void fold_range(u32x4& acc, const u32x4* __restrict__ src,
+                                           int64_t begin, int64_t end) {
   int64_t c = begin + threadIdx.x;
   for (; c + 7 * kThreads < end; c += 8 * kThreads) {
     u32x4 v[8];
@@ -126,12 +120,48 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __re
     for (int u = 0; u < 8; ++u) acc ^= v[u];
   }
   for (; c < end; c += kThreads) acc ^= __builtin_nontemporal_load(src + c);
+}
+
+// One word per workgroup, so the loads cannot be dropped.
+__device__ __forceinline__ void write_fold(const u32x4& acc, uint32_t* __restrict__ sink) {
+  __shared__ uint32_t red[kThreads / 64];
   uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x ^= __shfl_xor(x, off);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
   __syncthreads();
   if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+// Read-only stream: workgroup b reads the contiguous range
+// [b * per_wg, (b + 1) * per_wg) of 16-byte chunks once.
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __restrict__ src,
+                                                               int64_t chunks, int64_t per_wg,
+                                                               uint32_t* __restrict__ sink) {
+  const int64_t begin = (int64_t)blockIdx.x * per_wg;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  fold_range(acc, src, begin, begin + per_wg < chunks ? begin + per_wg : chunks);
+  write_fold(acc, sink);
+}
+
+// Re-read: the buffer is cut into gridDim.x ranges and in round r workgroup b
+// reads range (b + 8 r) mod gridDim.x, so every round reads each range once.
+// Workgroups go to the 8 XCDs round-robin (XCD b mod 8), so an XCD only ever
+// reads the ranges of its own residue class: a buffer of up to 8 L2s stays in
+// the XCDs' L2s, a larger one is served from the Infinity Cache (or HBM).
+// Consecutive rounds of one workgroup read different ranges, so the compute
+// unit's own L1 does not serve them.
+__global__ __launch_bounds__(kThreads) void stream_reread_kernel(const u32x4* __restrict__ src,
+                                                                 int64_t chunks, int64_t per_wg,
+                                                                 int32_t rounds,
+                                                                 uint32_t* __restrict__ sink) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int32_t r = 0; r < rounds; ++r) {
+    const int64_t rng = ((int64_t)blockIdx.x + 8LL * r) % gridDim.x;
+    const int64_t begin = rng * per_wg;
+    fold_range(acc, src, begin, begin + per_wg < chunks ? begin + per_wg : chunks);
+  }
+  write_fold(acc, sink);
 }
 
 }  // namespace
@@ -196,6 +226,16 @@ hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStrea
 }  // namespace pkv
 
 namespace pkv {
+
+hipError_t launch_stream_reread(const void* src, size_t bytes, int32_t rounds, uint32_t* sink,
+                                hipStream_t stream) {
+  const int64_t chunks = (int64_t)(bytes / 16);
+  if (chunks == 0 || rounds <= 0) return hipSuccess;
+  const int64_t per_wg = (chunks + kStreamReadWorkgroups - 1) / kStreamReadWorkgroups;
+  hipLaunchKernelGGL(stream_reread_kernel, dim3(kStreamReadWorkgroups), dim3(kThreads), 0, stream,
+                     static_cast<const u32x4*>(src), chunks, per_wg, rounds, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
   const int64_t chunks = (int64_t)(bytes / 16);

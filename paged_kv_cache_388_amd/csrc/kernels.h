@@ -148,5 +148,7 @@ hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStrea
 // sink: kStreamReadWorkgroups uint32 words, one per workgroup.
 constexpr int kStreamReadWorkgroups = 256 * 8;
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+hipError_t launch_stream_reread(const void* src, size_t bytes, int32_t rounds, uint32_t* sink,
+                                hipStream_t stream);
 
 }  // namespace pkv

@@ -6,12 +6,13 @@
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
 #include <atomic>
 #include <vector>
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
 #include "kernels.h"
 
@@ -102,10 +103,11 @@ size_t pool_block_bytes(const pkv_pool& pool) {
   return (size_t)pool.num_kv_heads * pool.block_size * pool.head_dim * elem_bytes(pool.dtype);
 }
 
+constexpr int kMaxDevices = 64;
+
 // Workgroups of the stream attention kernel on the current device: two per
 // compute unit (its occupancy), a multiple of the 8 XCDs.  Cached per device.
 int stream_workgroups() {
-  constexpr int kMaxDevices = 64;
   static std::atomic<int> cached[kMaxDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
@@ -120,6 +122,15 @@ int stream_workgroups() {
   return wgs;
 }
 
+// PAGEDKV_DECODE_PATH=grid in the environment sends every decode call (and
+// its workspace query) to the grid path: one workgroup per (kv head,
+// sequence, 512-token partition) and the partition merge, whatever the batch.
+// For measuring and testing that path at any shape; read on every call.
+bool force_grid_path() {
+  const char* v = getenv("PAGEDKV_DECODE_PATH");
+  return v && strcmp(v, "grid") == 0;
+}
+
 // Workgroups of the stream path for this call on the current device, or 0
 // where it cannot take the call: a batch above its LDS tables, or more
 // positions (kv heads x column groups x sub-tiles) than it indexes.  Decode
@@ -127,6 +138,7 @@ int stream_workgroups() {
 int32_t stream_wgs_for(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                        int32_t max_groups, bool multi) {
   if (num_seqs > (multi ? pkv::kMaxMultiSeqs : pkv::kMaxStreamSeqs)) return 0;
+  if (!multi && force_grid_path()) return 0;
   const long long subs = ((long long)(max_context_len > 0 ? max_context_len : 0) + pkv::kSubTokens - 1) /
                          pkv::kSubTokens;
   if ((long long)num_seqs * num_kv_heads * max_groups * subs > pkv::kMaxStreamPositions) return 0;
@@ -535,6 +547,18 @@ pkv_status pkv_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStr
     return fail(PKV_EINVAL, "src and byte count must be multiples of 16");
   hipError_t err = pkv::launch_stream_read(src, bytes, sink, stream);
   return err == hipSuccess ? PKV_OK : hip_fail(err, "pkv_stream_read launch");
+}
+
+pkv_status pkv_stream_reread(const void* src, size_t bytes, int32_t rounds, uint32_t* sink,
+                             hipStream_t stream) {
+  g_err[0] = '\0';
+  if (rounds < 0) return fail(PKV_EINVAL, "rounds %d < 0", rounds);
+  if (bytes == 0 || rounds == 0) return PKV_OK;
+  if (!src || !sink) return fail(PKV_EINVAL, "null pointer argument");
+  if (!aligned16(src) || (bytes & 15u))
+    return fail(PKV_EINVAL, "src and byte count must be multiples of 16");
+  hipError_t err = pkv::launch_stream_reread(src, bytes, rounds, sink, stream);
+  return err == hipSuccess ? PKV_OK : hip_fail(err, "pkv_stream_reread launch");
 }
 
 }  // extern "C"

@@ -48,13 +48,33 @@ def test_shared_blocks_count_once():
 
 
 def test_counter_traffic_follows_the_source(monkeypatch, tmp_path):
-    got = bench.counter_traffic("llama3_8b_gqa")
-    assert got is not None and got > bench.algorithmic_bytes(wl.llama3_8b_gqa()) * 0.99
-    assert bench.counter_traffic("no_such_workload") is None
-    other = tmp_path / "attention.hip"
-    other.write_text("// changed\n")
-    monkeypatch.setattr(bench, "ATTN_SOURCE", str(other))
-    assert bench.counter_traffic("llama3_8b_gqa") is None
+    """A counter summary counts only for the kernel source it was taken on."""
+    import hashlib
+    src = tmp_path / "attention.hip"
+    src.write_text("// kernel source\n")
+    sha = hashlib.sha256(src.read_bytes()).hexdigest()
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "attn_grid_kernel_long_ctx_bs16_hbm_counters.md").write_text(
+        f"# summary\n\ntraffic_bytes_per_call: 1234567\nsource_sha256: `{sha}`\n")
+    monkeypatch.setattr(bench, "ATTN_SOURCE", str(src))
+    monkeypatch.setattr(bench, "PROFILES", str(prof))
+    assert bench.counter_traffic("long_ctx_bs16", "attn_grid_kernel") == 1234567
+    assert bench.counter_traffic("long_ctx_bs16") is None             # another kernel's file
+    assert bench.counter_traffic("no_such_workload", "attn_grid_kernel") is None
+    src.write_text("// changed\n")
+    assert bench.counter_traffic("long_ctx_bs16", "attn_grid_kernel") is None
+
+
+def test_committed_counter_summaries_name_their_source():
+    """Every committed HBM counter summary carries the per-call traffic and
+    the SHA-256 of the source it was taken on."""
+    import glob
+    files = glob.glob(os.path.join(ROOT, "profiles", "*_hbm_counters.md"))
+    assert files
+    for path in files:
+        text = open(path).read()
+        assert "traffic_bytes_per_call:" in text and "source_sha256:" in text, path
 
 
 def test_more_than_one_gpu_is_refused():

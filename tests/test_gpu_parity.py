@@ -52,6 +52,18 @@ def test_edge_grid(dtype, D, bs, G):
     _run_and_check(_edge(dtype, D, bs, G), f"edge {dtype} D{D} bs{bs} G{G}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_edge_grid_on_partition_path(dtype, D, bs, G, monkeypatch):
+    """Every instantiation of the 512-token partition path (forced with
+    PAGEDKV_DECODE_PATH=grid): contexts on both sides of the partition and
+    sub-tile boundaries, NaN-poisoned pools."""
+    monkeypatch.setenv("PAGEDKV_DECODE_PATH", "grid")
+    _run_and_check(_edge(dtype, D, bs, G), f"partition path {dtype} D{D} bs{bs} G{G}")
+
+
 @pytest.mark.parametrize("G", [2, 3, 5, 16])
 def test_other_group_sizes(G):
     _run_and_check(_edge("bf16", 128, 16, G, H_kv=1, ctx=[7, 300, 700]), f"G{G}")
@@ -165,6 +177,26 @@ def test_repeat_runs_are_bit_identical():
     assert np.array_equal(a, b)
 
 
+def test_explicit_stream_argument_with_another_stream_current():
+    """stream= names the stream every kernel runs on, while another stream is
+    current; the workspace the binding allocates for itself belongs to that
+    stream."""
+    rng = np.random.default_rng(16)
+    w = wl.build("stream_arg", 16, rng, [600, 1200, 40, 0, 2000], 8, 2, 128, 16, "bf16",
+                 poison=True)
+    dw = DeviceWorkload(w)
+    side, other = torch.cuda.Stream(), torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    out = torch.empty_like(dw.q)
+    with torch.cuda.stream(other):
+        _lib.paged_kv_append(dw.new_key, dw.new_value, dw.k_cache, dw.v_cache, dw.slot_mapping,
+                             stream=side)
+        _lib.paged_attention_decode(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables,
+                                    dw.context_lens, w.scale, w.max_context_len, stream=side)
+    side.synchronize()
+    check_attention(to_host(out, "bf16"), oracle_step(w), "bf16", "stream= argument")
+
+
 def test_caller_stream_is_used():
     rng = np.random.default_rng(11)
     w = wl.build("stream", 11, rng, [600, 1200], 8, 2, 64, 16, "f16")
@@ -201,7 +233,46 @@ def test_batch_above_stream_limit_uses_grid_path():
     check_attention(out[sample], ref, "f16", "grid path sample")
 
 
-def test_single_sequence_many_partitions():
+def test_grid_path_long_context_shape_sampled():
+    """Above 4096 sequences the call takes the 512-token partition path by
+    itself.  The long-context workload's head shape (bf16, 64 query / 8 kv
+    heads, D 128, 32-token blocks) with mostly short contexts and one in 128
+    above 2048 tokens; sampled rows, all the long ones among them."""
+    rng = np.random.default_rng(17)
+    ctx = rng.integers(0, 21, size=4100)
+    ctx[::128] = rng.integers(2049, 2700, size=len(ctx[::128]))
+    w = wl.build("gridpath_long", 17, rng, ctx, 64, 8, 128, 32, "bf16", poison=True)
+    print(f"[gpu] grid path, long-context heads: B={w.num_seqs}", flush=True)
+    out = to_host(DeviceWorkload(w).step(), "bf16")
+    torch.cuda.synchronize()
+    sample = sorted(set(range(0, 4100, 128)) | set(np.random.default_rng(18).choice(4100, 60).tolist()))
+    check_attention(out[sample], oracle_step(w, seq_ids=sample), "bf16", "grid path long-context sample")
+
+
+def test_grid_path_f32_d128_sampled():
+    rng = np.random.default_rng(19)
+    ctx = rng.integers(0, 31, size=4150)
+    ctx[::101] = rng.integers(600, 1400, size=len(ctx[::101]))
+    w = wl.build("gridpath_f32", 19, rng, ctx, 8, 2, 128, 16, "f32", poison=True)
+    print(f"[gpu] grid path f32 D128: B={w.num_seqs}", flush=True)
+    out = to_host(DeviceWorkload(w).step(), "f32")
+    torch.cuda.synchronize()
+    sample = sorted(set(range(0, 4150, 101)) | set(np.random.default_rng(20).choice(4150, 80).tolist()))
+    check_attention(out[sample], oracle_step(w, seq_ids=sample), "f32", "grid path f32 sample")
+
+
+def test_single_long_sequence_split_over_waves():
+    """One 20000-token sequence on the stream path: its context is cut over
+    hundreds of waves and workgroups and merged in logical order."""
     rng = np.random.default_rng(13)
     w = wl.build("long1", 13, rng, [20000], 8, 1, 128, 32, "bf16", poison=True)
-    _run_and_check(w, "one long sequence")
+    _run_and_check(w, "one long sequence, stream path")
+
+
+def test_single_long_sequence_on_partition_path(monkeypatch):
+    """The same sequence on the 512-token partition path: 40 partitions and
+    their merge."""
+    monkeypatch.setenv("PAGEDKV_DECODE_PATH", "grid")
+    rng = np.random.default_rng(13)
+    w = wl.build("long1", 13, rng, [20000], 8, 1, 128, 32, "bf16", poison=True)
+    _run_and_check(w, "one long sequence, partition path")

@@ -124,3 +124,4 @@ def test_swap_rejects_bad_arguments(lib):
     assert inn(FAKE, 3, FAKE, FAKE, p, None, FAKE, entry, None) == 1        # no ids
     assert inn(FAKE, -4, FAKE, FAKE, p, FAKE, FAKE, entry, None) == 1
     assert inn(None, 0, None, None, p, None, None, 0, None) == 0
+
