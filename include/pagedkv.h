@@ -184,6 +184,41 @@ PKV_API pkv_status paged_attention_decode(void* out, const void* q,
                                           hipStream_t stream);
 
 /*
+ * paged_attention_decode_noalloc — paged_attention_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same computation, kernels and
+ * result, bit for bit, with the workspace taken from a scratch array the
+ * library holds in device memory, one per GPU, for the life of the process
+ * (paged_attention_noalloc_max_bytes() bytes, 32 MiB).  The caller passes
+ * only inputs and outputs; the arguments mean what they mean for
+ * paged_attention_decode.  The call allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine (its first call on a device looks
+ * up that device's copy of the array once).
+ *  - A call whose workspace (paged_attention_workspace_bytes of the same
+ *    shape) exceeds the scratch returns PKV_EWORKSPACE and enqueues nothing.
+ *    Every decode on the stream path fits (at most 25.6 MB on a 256-CU
+ *    device, at G = 16 and D = 128); a grid-path call above 4096 sequences
+ *    with long contexts may not.
+ *  - All calls on one GPU share its scratch, and the workspace needs no
+ *    initialisation: calls that overlap on one GPU (different streams or
+ *    threads with no ordering between them) race and give undefined
+ *    results.  Calls ordered on one stream are safe.
+ *  - Under PAGEDKV_CHECK=1 it returns PKV_EUNSUPPORTED: the metadata check
+ *    copies to host buffers and waits.
+ */
+PKV_API pkv_status paged_attention_decode_noalloc(void* out, const void* q,
+                                                  const void* k_cache, const void* v_cache,
+                                                  pkv_pool pool,
+                                                  const int32_t* block_tables,
+                                                  int32_t max_blocks_per_seq,
+                                                  const int32_t* context_lens,
+                                                  int32_t num_seqs, int32_t num_q_heads,
+                                                  float scale, int32_t max_context_len,
+                                                  hipStream_t stream);
+/* Bytes of the per-GPU scratch array behind paged_attention_decode_noalloc. */
+PKV_API size_t paged_attention_noalloc_max_bytes(void);
+
+/*
  * Bytes of workspace paged_attention_multi needs for this shape on the
  * current device, or 0 for invalid input, for a call it refuses, or for a
  * prefill-path call (max_query_len * G >= 64) that keeps each context whole.

@@ -53,6 +53,11 @@ def load():
     lib.paged_attention_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, PkvPool, c_vp, c_i32, c_vp,
                                            c_i32, c_i32, c_f, c_i32, c_vp, c_sz, c_vp]
     lib.paged_attention_decode.restype = c_i32
+    lib.paged_attention_decode_noalloc.argtypes = [c_vp, c_vp, c_vp, c_vp, PkvPool, c_vp, c_i32,
+                                                   c_vp, c_i32, c_i32, c_f, c_i32, c_vp]
+    lib.paged_attention_decode_noalloc.restype = c_i32
+    lib.paged_attention_noalloc_max_bytes.argtypes = []
+    lib.paged_attention_noalloc_max_bytes.restype = c_sz
     lib.paged_attention_multi_workspace_bytes.argtypes = [PkvPool, c_i32, c_i32, c_i32, c_i32]
     lib.paged_attention_multi_workspace_bytes.restype = c_sz
     lib.paged_attention_multi.argtypes = [c_vp, c_vp, c_vp, c_vp, PkvPool, c_vp, c_i32, c_vp, c_vp,
@@ -186,6 +191,34 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), pool, _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), B, Hq, float(scale), int(max_context_len),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def paged_attention_noalloc_max_bytes():
+    """Bytes of the per-GPU scratch array paged_attention_decode_noalloc uses."""
+    return int(load().paged_attention_noalloc_max_bytes())
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                   max_context_len, stream=None):
+    """paged_attention_decode with no workspace argument: the library takes
+    the workspace from its own per-GPU scratch array and allocates nothing.
+    Calls that overlap on one GPU share that array and race."""
+    pool = _pools(k_cache, v_cache)
+    dev = k_cache.device
+    _need(q, "q", dtype=k_cache.dtype, dim=3, device=dev)
+    _need(out, "out", dtype=k_cache.dtype, dim=3, device=dev)
+    if out.shape != q.shape or q.shape[2] != k_cache.shape[3]:
+        raise ValueError("q/out must be [B, H_q, D] with the pool's D")
+    _need(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _need(context_lens, "context_lens", dtype=torch.int32, dim=1, device=dev)
+    B, Hq, D = q.shape
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens disagree with q on num_seqs")
+    _check(load().paged_attention_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), pool, _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), B, Hq, float(scale), int(max_context_len),
+        _stream(stream)))
     return out
 
 

@@ -398,6 +398,84 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_cache,
                         workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Scratch of paged_attention_decode_noalloc: the decode workspace (sequence
+// offsets and the fp32 partial states of split sequences) for callers that
+// cannot allocate.  Each GPU the library runs on holds its own copy of the
+// array until the process ends.  On the host, `scratch` names a host-side
+// stand-in, never the device memory: only the address hipGetSymbolAddress
+// returns for the current device is passed to kernels.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of this GPU's scratch array, looked up once per device with
+// that device current, or nullptr (with the error set) if the lookup fails.
+void* scratch_on_current_device() {
+  static std::atomic<void*> cached[kMaxDevices];
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) {
+    hip_fail(err, "paged_attention_decode_noalloc: hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(PKV_EUNSUPPORTED, "paged_attention_decode_noalloc: device %d beyond the %d supported",
+         dev, kMaxDevices);
+    return nullptr;
+  }
+  void* ptr = cached[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || ptr == nullptr) {
+      hip_fail(err != hipSuccess ? err : hipErrorInvalidSymbol,
+               "paged_attention_decode_noalloc: hipGetSymbolAddress(scratch)");
+      return nullptr;
+    }
+    cached[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t paged_attention_noalloc_max_bytes(void) { return kScratchBytes; }
+
+pkv_status paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                          const void* v_cache, pkv_pool pool,
+                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t num_q_heads, float scale,
+                                          int32_t max_context_len, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (check_mode())
+    return fail(PKV_EUNSUPPORTED,
+                "paged_attention_decode_noalloc: PAGEDKV_CHECK=1 copies metadata into host "
+                "buffers and waits; use paged_attention_decode for checked calls");
+  // the size first: an oversized call is refused before any device call
+  const size_t need =
+      attention_workspace(pool, num_seqs, num_q_heads, 1, max_context_len, false);
+  if (need > kScratchBytes)
+    return fail(PKV_EWORKSPACE,
+                "paged_attention_decode_noalloc: this call needs %zu bytes of workspace, above "
+                "the %zu-byte scratch array (use paged_attention_decode with a workspace)",
+                need, kScratchBytes);
+  if (num_seqs <= 0 || need == 0)  // nothing to hold: validation alone decides
+    return attention_call("paged_attention_decode_noalloc launch", out, q, k_cache, v_cache, pool,
+                          block_tables, max_blocks_per_seq, context_lens, nullptr, num_seqs,
+                          num_q_heads, num_seqs, 1, scale, max_context_len, nullptr, 0, stream);
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return PKV_EHIP;
+  return attention_call("paged_attention_decode_noalloc launch", out, q, k_cache, v_cache, pool,
+                        block_tables, max_blocks_per_seq, context_lens, nullptr, num_seqs,
+                        num_q_heads, num_seqs, 1, scale, max_context_len, ws, kScratchBytes,
+                        stream);
+}
+
 size_t paged_attention_multi_workspace_bytes(pkv_pool pool, int32_t num_seqs, int32_t num_q_heads,
                                              int32_t max_query_len, int32_t max_context_len) {
   g_err[0] = '\0';

@@ -125,3 +125,18 @@ def test_swap_rejects_bad_arguments(lib):
     assert inn(FAKE, -4, FAKE, FAKE, p, FAKE, FAKE, entry, None) == 1
     assert inn(None, 0, None, None, p, None, None, 0, None) == 0
 
+
+def test_noalloc_refuses_calls_beyond_its_scratch(lib):
+    """The entry point for callers that cannot allocate holds its workspace in
+    a fixed 32 MiB array per GPU: a call needing more is refused before any
+    device call, with a message naming the sizes; bad scalars are refused as
+    in paged_attention_decode."""
+    call = lib.paged_attention_decode_noalloc
+    assert lib.paged_attention_noalloc_max_bytes() == 32 << 20
+    big = _pool(hkv=8, d=128)           # 5000 sequences: the partition path's fp32 states
+    assert call(FAKE, FAKE, FAKE, FAKE, big, FAKE, 2048, FAKE, 5000, 64, 0.1, 32768, None) == 3
+    assert b"scratch" in lib.pkv_last_error()
+    p = _pool()
+    assert call(FAKE, FAKE, FAKE, FAKE, p, FAKE, 4, FAKE, 2, 3, 0.1, 64, None) == 1  # H_q % H_kv
+    assert call(FAKE, FAKE, FAKE, FAKE, p, FAKE, 3, FAKE, 2, 2, 0.1, 64, None) == 1  # table too short
+    assert call(None, None, None, None, p, None, 0, None, 0, 2, 0.1, 0, None) == 0   # empty batch
