@@ -65,7 +65,15 @@ typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));  // cvt_pkrtz result
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Compile-time choice between the prefill path's two PV forms (see
+// softmax_pv_pair), passed to generic lambdas.
+template <bool B>
+struct ExactPV {
+  static constexpr bool value = B;
+};
 
 constexpr int kWaves = kStreamWaves;  // waves per workgroup, both paths
 constexpr int kThreads = 64 * kWaves;
@@ -394,7 +402,17 @@ __device__ __forceinline__ void qk_pair(const uint4 (&ka0)[N], const uint4 (&ka1
 }
 
 // Online softmax and PV of a sub-tile pair whose scores qk_pair produced.
-template <int DT, int N, int kMM>
+// Two forms of PV:
+//  - kExact = false: V arrives as fp16 (bf16 pools are converted when they
+//    are parked, exactly for magnitudes in [2^-14, 65504]) and P is rounded
+//    to the nearest fp16, one f16 MFMA per product.  P <= 2^8 under the lazy
+//    max, so it never overflows; its relative rounding error is at most
+//    2^-11, which bounds the error this adds to an output by
+//    2^-11 * sum_t p_t |v_t| / l.
+//  - kExact = true: V in its storage type and P split into hi + lo 16-bit
+//    parts, two MFMAs per product (~16 mantissa bits of P).  Taken where a
+//    bf16 V lies outside the fp16 range.
+template <int DT, int N, int kMM, bool kExact>
 __device__ __forceinline__ void softmax_pv_pair(const floatx4& S0, const floatx4& S1,
                                                 const u32x4 (&ve)[N], const u32x4 (&vo)[N],
                                                 bool mask, int valid0, int valid1,
@@ -435,6 +453,24 @@ __device__ __forceinline__ void softmax_pv_pair(const floatx4& S0, const floatx4
 #pragma unroll
   for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(__builtin_fmaf(sv[e], scale_log2, nmb));
   st.l += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+  static_assert(kMM == 2 * N, "16-bit types: two head-dim rows per V word");
+
+  if constexpr (!kExact) {
+    uint32_t ph[4];
+#pragma unroll
+    for (int q2 = 0; q2 < 4; ++q2)
+      ph[q2] = __builtin_bit_cast(uint32_t,
+                                  __builtin_convertvector(floatx2{pe[2 * q2], pe[2 * q2 + 1]}, halfx2));
+    const halfx8 P = __builtin_bit_cast(halfx8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+#pragma unroll
+    for (int wd = 0; wd < N; ++wd) {  // rows 2 wd and 2 wd + 1 of V^T, fp16
+      st.acc[2 * wd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, ve[wd]), P,
+                                                             st.acc[2 * wd], 0, 0, 0);
+      st.acc[2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, vo[wd]),
+                                                                 P, st.acc[2 * wd + 1], 0, 0, 0);
+    }
+    return;
+  }
 
   uint4 phi, plo;
   uint32_t* ph = reinterpret_cast<uint32_t*>(&phi);
@@ -453,7 +489,6 @@ __device__ __forceinline__ void softmax_pv_pair(const floatx4& S0, const floatx4
       pl[q2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p0 - (float)hh[0], p1 - (float)hh[1]));
     }
   }
-  static_assert(kMM == 2 * N, "16-bit types: two head-dim rows per V word");
 #pragma unroll
   for (int wd = 0; wd < N; ++wd) {
     const u32x4 ae = ve[wd], ao = vo[wd];  // rows 2 wd and 2 wd + 1 of V^T
@@ -1478,11 +1513,13 @@ void attn_prefill_kernel(AttnParams prm) {
   constexpr int kSwz = (4 * N - 1) < 15 ? (4 * N - 1) : 15;
   __shared__ __attribute__((aligned(16))) char sK[1][kWaves][kSubBytes];
   __shared__ __attribute__((aligned(16))) char sV[1][kWaves][kSubBytes];
+  __shared__ int sRedo;  // a wave found the fp16 PV form overflowed
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = uniform(tid >> 6);
   const int r = lane >> 4;
+  if (tid == 0) sRedo = 0;  // read after the stream's barriers
   // Workgroups are dispatched in linear id order, id i to XCD i % 8.  Inside
   // one grid row z (one sequence, kept in its dispatch slot) the ids are
   // dealt so that each (kv head, part) unit goes whole to one XCD, its column
@@ -1627,8 +1664,9 @@ void attn_prefill_kernel(AttnParams prm) {
   };
   // This wave's loaded sub-tile into slot w of stage buffer b: K chunk c of
   // token row t at chunk position c ^ (t & mask) (as restage_k stores it),
-  // V as the lanes hold it.
-  auto park = [&](const Tile<N>& t, int b) {
+  // V as the lanes hold it (bf16 V converted to fp16 for the fp16 PV form).
+  auto park = [&](const Tile<N>& t, int b, auto exact) {
+    constexpr bool kEx = decltype(exact)::value;
 #pragma unroll
     for (int kk = 0; kk < N; ++kk) {
       const int o = 1024 * kk + 16 * lane;
@@ -1647,10 +1685,24 @@ void attn_prefill_kernel(AttnParams prm) {
         // sub-tile's two words then the second's: attend_pair reads each
         // operand with one load.
         uint2 ev, od;
-        ev.x = __builtin_amdgcn_perm(t.v[1][qd], t.v[0][qd], 0x05040100u);
-        ev.y = __builtin_amdgcn_perm(t.v[3][qd], t.v[2][qd], 0x05040100u);
-        od.x = __builtin_amdgcn_perm(t.v[1][qd], t.v[0][qd], 0x07060302u);
-        od.y = __builtin_amdgcn_perm(t.v[3][qd], t.v[2][qd], 0x07060302u);
+        if constexpr (DT == DT_BF16 && !kEx) {
+          // bf16 -> fp32 is a shift of the bits; fp32 -> fp16 rounds to
+          // nearest (exact for every bf16 in the fp16 range; above it, +-inf)
+          auto f16x2 = [](uint32_t lo_bits, uint32_t hi_bits) {
+            return __builtin_bit_cast(
+                uint32_t, __builtin_convertvector(
+                              floatx2{__uint_as_float(lo_bits), __uint_as_float(hi_bits)}, halfx2));
+          };
+          ev.x = f16x2(t.v[0][qd] << 16, t.v[1][qd] << 16);
+          ev.y = f16x2(t.v[2][qd] << 16, t.v[3][qd] << 16);
+          od.x = f16x2(t.v[0][qd] & 0xffff0000u, t.v[1][qd] & 0xffff0000u);
+          od.y = f16x2(t.v[2][qd] & 0xffff0000u, t.v[3][qd] & 0xffff0000u);
+        } else {
+          ev.x = __builtin_amdgcn_perm(t.v[1][qd], t.v[0][qd], 0x05040100u);
+          ev.y = __builtin_amdgcn_perm(t.v[3][qd], t.v[2][qd], 0x05040100u);
+          od.x = __builtin_amdgcn_perm(t.v[1][qd], t.v[0][qd], 0x07060302u);
+          od.y = __builtin_amdgcn_perm(t.v[3][qd], t.v[2][qd], 0x07060302u);
+        }
         char* pair = &sV[b][w & ~1][0] + 8 * (w & 1);
         *reinterpret_cast<uint2*>(pair + ((2 * qd) * 64 + lane) * 16) = ev;
         *reinterpret_cast<uint2*>(pair + ((2 * qd + 1) * 64 + lane) * 16) = od;
@@ -1659,8 +1711,6 @@ void attn_prefill_kernel(AttnParams prm) {
   };
 
   WaveState<kMM> st[kGW];
-#pragma unroll
-  for (int g = 0; g < kGW; ++g) st[g].reset();
   // fp32 scales its logits directly.  16-bit types take |scale| (see above),
   // and a zero scale as the smallest normal float: every logit c * S is then
   // within 2^-24 of zero for |S| < 2^100, so every weight exp2(c * S - m)
@@ -1699,7 +1749,8 @@ void attn_prefill_kernel(AttnParams prm) {
   // used by both of the wave's groups (a pair whose second sub-tile is past
   // a group's limit masks it: every token there is past every column's
   // limit), four single sub-tiles for fp32.
-  auto compute_stage = [&](int sg, int b) {
+  auto compute_stage = [&](int sg, int b, auto exact) {
+    constexpr bool kEx = decltype(exact)::value;
     if constexpr (DT != DT_F32) {
 #pragma unroll
       for (int j = 0; j < kWaves; j += 2) {
@@ -1717,8 +1768,8 @@ void attn_prefill_kernel(AttnParams prm) {
 #pragma unroll
           for (int g = 0; g < kGW; ++g) {
             const bool mask = (sub + 2) * kSub > vis_first[g];
-            softmax_pv_pair<DT, N, kMM>(S[g][0], S[g][1], ve, vo, mask, valid_of(g, sub),
-                                        valid_of(g, sub + 1), scale_log2, r, st[g]);
+            softmax_pv_pair<DT, N, kMM, kEx>(S[g][0], S[g][1], ve, vo, mask, valid_of(g, sub),
+                                             valid_of(g, sub + 1), scale_log2, r, st[g]);
           }
         }
       }
@@ -1749,16 +1800,37 @@ void attn_prefill_kernel(AttnParams prm) {
   // buffer (whose last readers finished before the previous barrier).  (A
   // ring of three tiles measured no faster: the core, not the loads, sets
   // the pace.)
-  Tile<N> t;
-  load_sub(t, st0 * kWaves + w);
-  park(t, 0);
-  __syncthreads();
-  for (int sg = st0; sg < st1; ++sg) {
-    load_sub(t, (sg + 1) * kWaves + w);
-    compute_stage(sg, 0);
-    __syncthreads();  // every wave has read the stage
-    park(t, 0);
+  auto stream_context = [&](auto exact) {
+#pragma unroll
+    for (int g = 0; g < kGW; ++g) st[g].reset();
+    Tile<N> t;
+    load_sub(t, st0 * kWaves + w);
+    park(t, 0, exact);
     __syncthreads();
+    for (int sg = st0; sg < st1; ++sg) {
+      load_sub(t, (sg + 1) * kWaves + w);
+      compute_stage(sg, 0, exact);
+      __syncthreads();  // every wave has read the stage
+      park(t, 0, exact);
+      __syncthreads();
+    }
+  };
+  // 16-bit types take the fp16 PV form.  A bf16 V element beyond the fp16
+  // range became +-inf there, which leaves some accumulator of the
+  // workgroup non-finite (inf * p, or 0 * inf = NaN where p = 0), so the
+  // workgroup then streams its context again in the exact form (as it does,
+  // at no harm but the time, for non-finite inputs).
+  stream_context(ExactPV<DT == DT_F32>{});
+  if constexpr (DT == DT_BF16) {
+    float sum = 0.f;
+#pragma unroll
+    for (int g = 0; g < kGW; ++g)
+#pragma unroll
+      for (int mm = 0; mm < kMM; ++mm) sum += (st[g].acc[mm][0] + st[g].acc[mm][1]) + (st[g].acc[mm][2] + st[g].acc[mm][3]);
+    const bool bad = !(sum - sum == 0.f);  // inf - inf and NaN - NaN are NaN
+    if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) sRedo = 1;
+    __syncthreads();
+    if (sRedo) stream_context(ExactPV<true>{});
   }
 
 

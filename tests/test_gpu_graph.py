@@ -12,10 +12,9 @@ import numpy as np
 import pytest
 import torch
 
-from paged_kv_cache_388_amd import _lib
 from paged_kv_cache_388_amd import workloads as wl
 
-from gpu_common import DeviceWorkload, check_attention, oracle_step, to_host
+from gpu_common import DeviceWorkload, check_step, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +24,7 @@ def _graph_vs_eager(w, what):
     dw = DeviceWorkload(w)
     eager = to_host(dw.step(), w.dtype)       # also caches the device's grid size
     torch.cuda.synchronize()
-    check_attention(eager, oracle_step(w), w.dtype, what)
+    check_step(eager, w, what)
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())

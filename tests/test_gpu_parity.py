@@ -15,7 +15,7 @@ from paged_kv_cache_388_amd import _lib
 from paged_kv_cache_388_amd import workloads as wl
 
 from gpu_common import (DeviceWorkload, check_attention, oracle_pools_after_step, oracle_step,
-                        to_dev, to_host)
+                        to_host)
 
 pytestmark = pytest.mark.gpu
 

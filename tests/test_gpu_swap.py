@@ -10,7 +10,7 @@ import oracle
 from paged_kv_cache_388_amd import _lib
 from paged_kv_cache_388_amd import workloads as wl
 
-from gpu_common import TORCH_DT, to_dev, to_host
+from gpu_common import to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
