@@ -79,6 +79,24 @@ def unique_kv_bytes(w):
     return 2 * sum(fill.values()) * w.num_kv_heads * w.head_dim * b
 
 
+def shared_block_bytes(w):
+    """Bytes of K and V held by the physical blocks that more than one
+    sequence reads, and the mean number of sequences reading each of them."""
+    b = wl.ELEM_BYTES[w.dtype]
+    refs, fill = {}, {}
+    for s in range(w.num_seqs):
+        n = int(w.context_lens[s])
+        for j in range((n + w.block_size - 1) // w.block_size):
+            blk = int(w.block_tables[s, j])
+            refs[blk] = refs.get(blk, 0) + 1
+            fill[blk] = max(fill.get(blk, 0), min(w.block_size, n - j * w.block_size))
+    shared = [blk for blk, k in refs.items() if k > 1]
+    if not shared:
+        return 0, 0.0
+    nbytes = 2 * sum(fill[blk] for blk in shared) * w.num_kv_heads * w.head_dim * b
+    return nbytes, sum(refs[blk] for blk in shared) / len(shared)
+
+
 def attention_flops(w):
     """QK and PV multiply-adds of one call: 4 * D flops per (new token, query
     head, visible context token)."""
@@ -509,16 +527,17 @@ def read_probe(mib, steps, warmup):
                       "read_GBps": round(n / (ms * 1e-3) / 1e9, 1)}))
 
 
-def reread_probe(mib, rounds, steps, warmup):
-    """Time the library's re-read probe: a buffer of `mib` MiB read `rounds`
-    times per call, each XCD re-reading only its own eighth.  Up to 8 L2s
-    (32 MiB) the re-reads come from the XCDs' L2s, above that from the
-    Infinity Cache: the cache-side read ceilings that a decode over blocks
-    shared between sequences runs against."""
+def reread_rate(nbytes, rounds, steps, warmup):
+    """Mean duration (ms) of the library's re-read probe over a buffer of
+    nbytes read `rounds` times per call, each XCD re-reading only its own
+    eighth, and the rate in GB/s.  Up to 8 L2s (32 MiB) the re-reads come
+    from the XCDs' L2s, above that from the Infinity Cache: the cache-side
+    read ceilings that a decode over blocks shared between sequences runs
+    against."""
     import torch
     from paged_kv_cache_388_amd import _lib
     _lib.load()
-    n = int(mib * (1 << 20)) // 16 * 16
+    n = max(16, int(nbytes) // 16 * 16)
     src = torch.empty(n, dtype=torch.uint8, device="cuda")
     src.random_(0, 255)
     sink = torch.zeros(_lib.STREAM_READ_WORKGROUPS, dtype=torch.int32, device="cuda")
@@ -534,8 +553,14 @@ def reread_probe(mib, rounds, steps, warmup):
         b[i].record(stream)
     torch.cuda.synchronize()
     ms = float(np.mean([x.elapsed_time(y) for x, y in zip(a, b)]))
+    return n, ms, n * rounds / (ms * 1e-3) / 1e9
+
+
+def reread_probe(mib, rounds, steps, warmup):
+    """Print the re-read probe's rate for a buffer of `mib` MiB."""
+    n, ms, gbs = reread_rate(mib * (1 << 20), rounds, steps, warmup)
     print(json.dumps({"reread_probe_bytes": n, "rounds": rounds, "ms_per_call": round(ms, 4),
-                      "read_GBps": round(n * rounds / (ms * 1e-3) / 1e9, 1)}))
+                      "read_GBps": round(gbs, 1)}))
 
 
 def main():
@@ -760,6 +785,19 @@ def main():
         alg = alg - kv + uniq
     achieved = alg / (attn_avg_ms * 1e-3) / 1e9
     flops = attention_flops(w)
+    l2 = None
+    if shared and not w.multi:
+        # blocks read by many sequences are served by the L2 of the XCD that
+        # streams their kv head: the ceiling is the L2 re-read rate over a
+        # buffer of the shared blocks' size, read as many times as they are
+        sb, reads = shared_block_bytes(w)
+        rounds = max(1, int(round(reads)))
+        _, l2_ms, l2_gbs = reread_rate(sb, rounds, 10, 2)
+        logical = algorithmic_bytes(w)
+        l2 = {"shared_block_bytes": sb, "reads_per_shared_block": round(reads, 2),
+              "probe_rounds": rounds, "probe_GBps": round(l2_gbs, 1),
+              "logical_bytes_per_launch": logical,
+              "logical_GBps": round(logical / (attn_avg_ms * 1e-3) / 1e9, 1)}
     G = w.num_q_heads // w.num_kv_heads
     if w.multi and w.max_query_len * G >= PREFILL_MIN_COLS:
         # the prefill path reads each context once per 64 columns and does
@@ -775,6 +813,22 @@ def main():
                     "algorithmic_flops_per_launch": flops,
                     "algorithmic_bytes_per_launch": alg,
                     "hbm_GBps_of_algorithmic_bytes": round(achieved, 1)}
+    elif l2 is not None:
+        # shared blocks: not HBM-bound; every logical byte passes through L2
+        roofline = {"bound": "l2", "achieved": l2["logical_GBps"], "peak": l2["probe_GBps"],
+                    "unit": "GB/s", "frac": round(l2["logical_GBps"] / l2["probe_GBps"], 4),
+                    "traffic": None,
+                    "peak_source": ("measured in this run: pkv_stream_reread over the shared "
+                                    "blocks' bytes, as many rounds as each is read (no "
+                                    "published L2 figure)"),
+                    "kernel": (f"attn_stream_kernel<{w.dtype},{w.head_dim},{w.block_size}> + "
+                               "attn_stream_merge_kernel (one paged_attention_decode call)"),
+                    "algorithmic_bytes_per_launch": l2["logical_bytes_per_launch"],
+                    "kv_bytes_unique": uniq,
+                    "unique_bytes_GBps": round(achieved, 1),
+                    "unique_frac_of_hbm_peak": round(achieved / PEAK_HBM_GBS, 4),
+                    **{k: l2[k] for k in ("shared_block_bytes", "reads_per_shared_block",
+                                          "probe_rounds")}}
     else:
         grid = args.decode_path == "grid" and not w.multi
         kname = "attn_grid_kernel" if grid else "attn_stream_kernel"

@@ -83,3 +83,14 @@ def test_more_than_one_gpu_is_refused():
     assert res.returncode == 2
     assert "one GPU" in res.stderr
     assert res.stdout == ""
+
+
+def test_shared_block_bytes_by_hand():
+    """A 100-token prefix at 16-token blocks: 6 full blocks shared by every
+    sequence (the 7th, partly filled, is copied per sequence), each read by
+    all 4 sequences; nothing is shared in a private-table workload."""
+    w = wl.shared_prefix(num_seqs=4, prefix_tokens=100)
+    sb, reads = bench.shared_block_bytes(w)
+    assert reads == 4
+    assert sb == 2 * 6 * 16 * w.num_kv_heads * w.head_dim * 2
+    assert bench.shared_block_bytes(wl.tiny_f32()) == (0, 0.0)
