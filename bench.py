@@ -47,7 +47,10 @@ CPU_PROCESS_CAP = 16
 # dense MFMA peaks of MI355X, TFLOP/s, by the dtype the products run in
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 PREFILL_MIN_COLS = 64      # max_query_len * G at which a multi call takes the prefill path
-ATTN_SOURCE = os.path.join(ROOT, "paged_kv_cache_388_amd", "csrc", "attention.hip")
+# the sources the decode kernels compile from; counter summaries record the
+# SHA-256 of their contents in this order
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_388_amd", "csrc", f)
+                  for f in ("attention.hip", "attn_common.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) and seqs/s"
 
@@ -108,12 +111,21 @@ def attention_flops(w):
     return 4 * w.head_dim * G * w.num_kv_heads * visible
 
 
+def decode_source_sha():
+    """SHA-256 of the decode kernels' sources, concatenated in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in DECODE_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def counter_traffic(workload, kernel="attn_stream_kernel"):
     """HBM bytes per attention call from the committed counter summary of this
     kernel and workload, or None if there is none or the kernel source has
     changed since the counters were taken (the summary records the source's
     SHA-256)."""
-    import hashlib
     path = os.path.join(PROFILES, f"{kernel}_{workload}_hbm_counters.md")
     if not os.path.exists(path):
         return None
@@ -123,9 +135,7 @@ def counter_traffic(workload, kernel="attn_stream_kernel"):
             if ":" in line and line.strip().startswith(("traffic_bytes_per_call", "source_sha256")):
                 k, v = line.strip().split(":", 1)
                 fields[k.strip()] = v.strip().strip("`")
-    with open(ATTN_SOURCE, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if fields.get("source_sha256") != sha or "traffic_bytes_per_call" not in fields:
+    if fields.get("source_sha256") != decode_source_sha() or "traffic_bytes_per_call" not in fields:
         return None
     return int(fields["traffic_bytes_per_call"])
 
@@ -595,6 +605,10 @@ def main():
                     help="grid: every decode call takes the 512-token partition path (one "
                          "workgroup per (kv head, sequence, partition) and the partition "
                          "merge; PAGEDKV_DECODE_PATH=grid) instead of the stream path")
+    ap.add_argument("--k-load", choices=("lines", "direct"), default="lines",
+                    help="direct: stream-path decode of bf16 / D 128 / 16-token blocks loads K "
+                         "straight in the matrix-core operand order instead of whole lines "
+                         "re-dealt through LDS (PAGEDKV_K_LOAD=direct; a measurement variant)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step as one captured HIP graph (the attention call's "
                          "events are then taken in a loop of their own)")
@@ -633,6 +647,8 @@ def main():
 
     if args.decode_path == "grid":
         os.environ["PAGEDKV_DECODE_PATH"] = "grid"   # read by the library on every call
+    if args.k_load == "direct":
+        os.environ["PAGEDKV_K_LOAD"] = "direct"
     t_gen = time.perf_counter()
     w = wl.named(args.workload)
     print(f"[bench] workload {w.name} generated in {time.perf_counter() - t_gen:.1f} s",
@@ -869,7 +885,8 @@ def main():
                    "new_tokens": int(w.q.shape[0]),
                    "parallelism": "single GPU", "cold": bool(args.cold),
                    "graph": bool(args.graph),
-                   **({"decode_path": args.decode_path} if not w.multi else {})},
+                   **({"decode_path": args.decode_path, "k_load": args.k_load}
+                      if not w.multi else {})},
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "seqs_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "new_tokens_per_s": round(w.q.shape[0] / (ms_per_step * 1e-3), 1),

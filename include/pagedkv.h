@@ -128,7 +128,10 @@ PKV_API pkv_status paged_kv_append(const void* key, const void* value,
  * every decode call and this query take the grid path (one workgroup per
  * (kv head, sequence, 512-token partition), then the partition merge)
  * whatever the batch.  Read on every call; the query and the call must see
- * the same setting.
+ * the same setting.  PAGEDKV_K_LOAD=direct, likewise for measurement only:
+ * stream-path decode calls of one shape (bf16, head_dim 128, block_size 16)
+ * load K straight in the matrix-core operand order instead of whole
+ * 128-byte lines re-dealt through LDS; the result is the same bit for bit.
  */
 PKV_API size_t paged_attention_workspace_bytes(pkv_pool pool, int32_t num_seqs,
                                                int32_t num_q_heads, int32_t max_context_len);

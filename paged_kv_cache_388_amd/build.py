@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libpagedkv.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["attention.hip", "cache_ops.hip", "pagedkv_api.cpp", "block_manager.cpp"]
+SOURCES = ["attention.hip", "prefill.hip", "cache_ops.hip", "pagedkv_api.cpp", "block_manager.cpp"]
 ARCH = "gfx950"
 
 

@@ -94,6 +94,10 @@ struct AttnParams {
   int32_t prefill_parts;
   // Prefill path: column groups per wave (1 or 2; see prefill_plan).
   int32_t prefill_wave_groups;
+  // Decode on the stream path, measurement variant: 1 = K loaded straight in
+  // the MFMA operand order instead of whole lines re-dealt through LDS
+  // (built for bf16, D 128, 16-token blocks only; ignored elsewhere).
+  int32_t k_direct;
 };
 
 // Workspace layout of one decode call, shared by the size query and the call.
@@ -122,9 +126,13 @@ AttnWorkspace prefill_workspace_layout(int32_t num_query_tokens, int32_t num_q_h
                                        int32_t head_dim, int32_t parts);
 
 // dtype: 0 f32, 1 f16, 2 bf16.  Returns hipErrorInvalidValue for a (dtype,
-// head_dim, block_size) combination that is not instantiated.
+// head_dim, block_size) combination that is not instantiated.  Calls with
+// prefill_blocks > 0 go to launch_prefill.
 hipError_t launch_paged_attention(const AttnParams& p, int dtype, int head_dim,
                                   int block_size, hipStream_t stream);
+// The prefill path (prefill.hip).
+hipError_t launch_prefill(const AttnParams& p, int dtype, int head_dim, int block_size,
+                          hipStream_t stream);
 
 hipError_t launch_kv_append(const void* key, const void* value, void* k_cache,
                             void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,

@@ -131,6 +131,15 @@ bool force_grid_path() {
   return v && strcmp(v, "grid") == 0;
 }
 
+// PAGEDKV_K_LOAD=direct: decode calls on the stream path load K straight in
+// the MFMA operand order instead of whole 128-byte lines re-dealt through
+// LDS.  A measurement variant of one shape (bf16, D 128, 16-token blocks),
+// ignored elsewhere; same result bit for bit.  Read on every call.
+bool k_direct_loads() {
+  const char* v = getenv("PAGEDKV_K_LOAD");
+  return v && strcmp(v, "direct") == 0;
+}
+
 // Workgroups of the stream path for this call on the current device, or 0
 // where it cannot take the call: a batch above its LDS tables, or more
 // positions (kv heads x column groups x sub-tiles) than it indexes.  Decode
@@ -371,6 +380,7 @@ pkv_status attention_call(const char* what, void* out, const void* q, const void
   prm.prefill_blocks = pf_blocks;
   prm.prefill_parts = pf_parts;
   prm.prefill_wave_groups = plan.wave_groups;
+  prm.k_direct = !multi && k_direct_loads() ? 1 : 0;
   hipError_t err = pkv::launch_paged_attention(prm, pool.dtype, pool.head_dim, pool.block_size, stream);
   return err == hipSuccess ? PKV_OK : hip_fail(err, what);
 }

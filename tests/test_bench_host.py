@@ -52,17 +52,19 @@ def test_counter_traffic_follows_the_source(monkeypatch, tmp_path):
     import hashlib
     src = tmp_path / "attention.hip"
     src.write_text("// kernel source\n")
-    sha = hashlib.sha256(src.read_bytes()).hexdigest()
+    common = tmp_path / "attn_common.h"
+    common.write_text("// shared device code\n")
+    sha = hashlib.sha256(src.read_bytes() + common.read_bytes()).hexdigest()
     prof = tmp_path / "profiles"
     prof.mkdir()
     (prof / "attn_grid_kernel_long_ctx_bs16_hbm_counters.md").write_text(
         f"# summary\n\ntraffic_bytes_per_call: 1234567\nsource_sha256: `{sha}`\n")
-    monkeypatch.setattr(bench, "ATTN_SOURCE", str(src))
+    monkeypatch.setattr(bench, "DECODE_SOURCES", [str(src), str(common)])
     monkeypatch.setattr(bench, "PROFILES", str(prof))
     assert bench.counter_traffic("long_ctx_bs16", "attn_grid_kernel") == 1234567
     assert bench.counter_traffic("long_ctx_bs16") is None             # another kernel's file
     assert bench.counter_traffic("no_such_workload", "attn_grid_kernel") is None
-    src.write_text("// changed\n")
+    common.write_text("// changed\n")
     assert bench.counter_traffic("long_ctx_bs16", "attn_grid_kernel") is None
 
 

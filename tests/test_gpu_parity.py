@@ -276,3 +276,17 @@ def test_single_long_sequence_on_partition_path(monkeypatch):
     rng = np.random.default_rng(13)
     w = wl.build("long1", 13, rng, [20000], 8, 1, 128, 32, "bf16", poison=True)
     _run_and_check(w, "one long sequence, partition path")
+
+
+def test_direct_k_load_variant_is_bit_identical(monkeypatch):
+    """PAGEDKV_K_LOAD=direct (the measurement variant that loads K straight in
+    the matrix-core operand order, bf16 / D 128 / 16-token blocks) gives the
+    default kernel's output bit for bit, and so the oracle's within the bar."""
+    rng = np.random.default_rng(21)
+    w = wl.build("kdirect", 21, rng, [1, 15, 17, 300, 2000, 4100, 0, 700], 32, 8, 128, 16, "bf16",
+                 poison=True)
+    base = to_host(DeviceWorkload(w).step(), "bf16")
+    monkeypatch.setenv("PAGEDKV_K_LOAD", "direct")
+    direct = to_host(DeviceWorkload(w).step(), "bf16")
+    assert np.array_equal(base, direct)
+    check_attention(direct, oracle_step(w), "bf16", "direct K loads")
