@@ -551,25 +551,10 @@ void attn_prefill_kernel(AttnParams prm) {
   }
 }
 
-// Merge of a split prefill context for one (query row, query head): one
-// wave, lanes over the head dim, parts in order.  Grid: sequence x new token
-// (up to max_query_len) x query head, a wave each, four per workgroup.  The
-// number of non-empty parts follows from the same stage counts the prefill
-// kernel uses.
-template <int DT, int D>
-__global__ __launch_bounds__(kThreads) void attn_prefill_merge_kernel(AttnParams prm) {
-  const int lane = threadIdx.x & 63;
-  const long long id = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int Hq = prm.num_q_heads;
-  const int G = prm.group;
-  const int P = prm.prefill_parts;
-  const int hq = (int)(id % Hq);
-  const long long rest = id / Hq;
-  const int i = (int)(rest % prm.max_query_len);
-  const int s = (int)(rest / prm.max_query_len);
-  if (s >= prm.num_seqs) return;
-  int n = prm.context_lens[s];
-  n = n < 0 ? 0 : (n > prm.max_context_len ? prm.max_context_len : n);
+// New tokens of sequence s with a context of n tokens, clamped as every
+// kernel clamps them: [query_start[s], query_start[s+1]) inside [0, rows],
+// at most min(n, max_query_len).
+__device__ __forceinline__ int clamped_new_tokens(const AttnParams& prm, int s, int n, int* q0_out) {
   const int T = prm.num_query_tokens;
   int q0 = prm.query_start[s], qe = prm.query_start[s + 1];
   q0 = q0 < 0 ? 0 : (q0 > T ? T : q0);
@@ -577,7 +562,65 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_merge_kernel(AttnParams
   int L = qe - q0;
   L = L < n ? L : n;
   L = L < prm.max_query_len ? L : prm.max_query_len;
+  if (q0_out) *q0_out = q0;
+  return L;
+}
+
+// Merge of split prefill contexts: eight (query row, query head) items per
+// wave, eight lanes per item, each lane D / 8 of the head dim, parts in
+// order: each lane sums its values over the parts exactly as a whole wave
+// per item did, with eight times fewer waves.  Items past a sequence's rows
+// exit at once.  The number of non-empty parts follows from the same stage
+// counts the prefill kernel uses.  Grid: one thread per (item, lane).
+constexpr int kMergeLanes = 8;
+
+template <int DT, int NV>
+__device__ __forceinline__ void store_vals(void* dst, const float (&o)[NV]) {
+  if constexpr (DT == DT_F32) {
+#pragma unroll
+    for (int i = 0; i < NV / 4; ++i)
+      reinterpret_cast<float4*>(dst)[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+  } else {
+    uint32_t packed[NV / 2];
+#pragma unroll
+    for (int i = 0; i < NV / 2; ++i) {
+      uint16_t lo, hi;
+      if constexpr (DT == DT_F16) {
+        lo = __builtin_bit_cast(uint16_t, (_Float16)o[2 * i]);
+        hi = __builtin_bit_cast(uint16_t, (_Float16)o[2 * i + 1]);
+      } else {
+        lo = f32_to_bf16_rne(o[2 * i]);
+        hi = f32_to_bf16_rne(o[2 * i + 1]);
+      }
+      packed[i] = (uint32_t)lo | ((uint32_t)hi << 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NV / 8; ++i)
+      reinterpret_cast<uint4*>(dst)[i] =
+          make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
+  }
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void attn_prefill_merge_kernel(AttnParams prm) {
+  constexpr int kF = D / kMergeLanes;  // head-dim values per lane
+  const long long item = ((long long)blockIdx.x * kThreads + threadIdx.x) / kMergeLanes;
+  const int sub = (int)(threadIdx.x % kMergeLanes);
+  const int Hq = prm.num_q_heads;
+  const int G = prm.group;
+  const int P = prm.prefill_parts;
+  const int hq = (int)(item % Hq);
+  const long long rest = item / Hq;
+  const int i = (int)(rest % prm.max_query_len);
+  const long long sl = rest / prm.max_query_len;
+  if (sl >= prm.num_seqs) return;
+  const int s = (int)sl;
+  int n = prm.context_lens[s];
+  n = n < 0 ? 0 : (n > prm.max_context_len ? prm.max_context_len : n);
+  int q0;
+  const int L = clamped_new_tokens(prm, s, n, &q0);
   if (i >= L) return;
+  const int Ps = P;
   const int kGB = kWaves * prm.prefill_wave_groups;  // groups per column block
   const int c = i * G + hq % G;  // the column, in its kv head's block
   const int cb = c / (kGB * kSub);
@@ -587,30 +630,35 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_merge_kernel(AttnParams
   i_last = i_last < L - 1 ? i_last : L - 1;
   const int rows_b = n - L + i_last + 1;
   const int nstage_all = ((rows_b + kSub - 1) / kSub + kWaves - 1) / kWaves;
-  const int per_part = (nstage_all + P - 1) / P;
+  const int per_part = (nstage_all + Ps - 1) / Ps;
   const int nparts = (nstage_all + per_part - 1) / per_part;
   const size_t base = ((size_t)(q0 + i) * Hq + hq) * P;
-  constexpr int kPer = D / 64;
 
   float M = kNegInf;
-  for (int k = lane; k < nparts; k += 64) M = fmaxf(M, prm.part_ml[(base + k) * 2]);
+  for (int k = 0; k < nparts; ++k) M = fmaxf(M, prm.part_ml[(base + k) * 2]);
+  float o[kF];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float o[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) o[j] = 0.f;
+  for (int j = 0; j < kF; ++j) o[j] = 0.f;
   float lsum = 0.f;
   for (int k = 0; k < nparts; ++k) {
     const float2 ml = *reinterpret_cast<const float2*>(prm.part_ml + (base + k) * 2);
     const float f = ml.x == kNegInf ? 0.f : fast_exp2(ml.x - M);
     lsum += f * ml.y;
+    const float4* src = reinterpret_cast<const float4*>(prm.part_o + (base + k) * D + sub * kF);
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) o[j] += f * prm.part_o[(base + k) * D + lane + 64 * j];
+    for (int j = 0; j < kF / 4; ++j) {
+      const float4 x = src[j];
+      o[4 * j] += f * x.x;
+      o[4 * j + 1] += f * x.y;
+      o[4 * j + 2] += f * x.z;
+      o[4 * j + 3] += f * x.w;
+    }
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  const size_t orow = ((size_t)(q0 + i) * Hq + hq) * D;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) store_out<DT>(prm.out, orow + lane + 64 * j, o[j] * inv);
+  for (int j = 0; j < kF; ++j) o[j] *= inv;
+  const size_t orow = ((size_t)(q0 + i) * Hq + hq) * D + (size_t)sub * kF;
+  store_vals<DT, kF>(static_cast<char*>(prm.out) + orow * Elem<DT>::bytes, o);
 }
 
 template <int DT, int D, int BS>
@@ -632,8 +680,9 @@ hipError_t launch_prefill_typed(const AttnParams& prm, hipStream_t stream) {
       return hipErrorInvalidValue;
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || prm.prefill_parts == 1) return err;
-    const long long waves = (long long)prm.num_seqs * prm.max_query_len * prm.num_q_heads;
-    const long long nm = (waves + kWaves - 1) / kWaves;
+    const long long threads =
+        (long long)prm.num_seqs * prm.max_query_len * prm.num_q_heads * kMergeLanes;
+    const long long nm = (threads + kThreads - 1) / kThreads;
     if (nm > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((attn_prefill_merge_kernel<DT, D>), dim3((unsigned)nm), block, 0, stream,
                        prm);
