@@ -38,6 +38,22 @@ struct ExactPV {
 // the pair per case made the compiler move all of them at every join).
 constexpr float kLazyLog2 = 8.f;
 
+// When a pair may skip the column max.  A pair first weighs its tokens
+// against the column's current reference m; only if some lane's weight
+// exceeds thr (or is NaN) does it take the column max and apply the lazy
+// rule above, then weigh the tokens again.  With a
+// finite |m| < 2^22, thr = 16: a column the rule would move has a logit
+// above m + 8 up to rounding (above m + 7.5 at that magnitude), whose
+// weight is then above 16, so skipping changes nothing.  Without a usable
+// reference thr = -1 (always look), except that a padding column (q = 0) with
+// none looks once any weight is positive, that is at its first unmasked pair.
+struct PairRef {
+  float thr;
+  __device__ __forceinline__ void set(float m, bool real) {
+    thr = __builtin_fabsf(m) < 0x1p22f ? 16.f : (m == kNegInf && !real ? 0.f : -1.f);
+  }
+};
+
 // QK of a sub-tile pair: two independent MFMA chains.  Issued ahead of the
 // softmax of an earlier product, the MFMAs run while the VALU works on it
 // (the softmax's rescale branch would otherwise end the scheduling region
@@ -79,7 +95,8 @@ template <int DT, int N, int kMM, bool kExact>
 __device__ __forceinline__ void softmax_pv_pair(const floatx4& S0, const floatx4& S1,
                                                 const u32x4 (&ve)[N], const u32x4 (&vo)[N],
                                                 bool mask, int valid0, int valid1,
-                                                float scale_log2, int r, WaveState<kMM>& st) {
+                                                float scale_log2, int r, WaveState<kMM>& st,
+                                                PairRef& ref, bool real) {
   static_assert(DT != DT_F32, "16-bit types only");
   // Raw scores S; the logit is c * S with c = scale_log2 > 0 (a negative
   // scale arrives as a negated query, a zero one as the smallest normal
@@ -100,21 +117,28 @@ __device__ __forceinline__ void softmax_pv_pair(const floatx4& S0, const floatx4
     }
   }
   const auto mx = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
-  const float mloc =
-      scale_log2 * rows_max(mx(mx(mx(sv[0], sv[1]), mx(sv[2], sv[3])), mx(mx(sv[4], sv[5]), mx(sv[6], sv[7]))));
-  const bool move = mloc > st.m + kLazyLog2;  // -inf > -inf is false: a fully masked column stays
-  if (__builtin_amdgcn_ballot_w64(move)) {
-    const float m_new = move ? mloc : st.m;
-    const float alpha = move ? fast_exp2(st.m - m_new) : 1.f;
-    st.l *= alpha;
-#pragma unroll
-    for (int mm = 0; mm < kMM; ++mm) st.acc[mm] *= alpha;
-    st.m = m_new;
-  }
-  const float nmb = st.m == kNegInf ? 0.f : -st.m;
   float pe[8];
+  const float nmb = st.m == kNegInf ? 0.f : -st.m;
 #pragma unroll
   for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(__builtin_fmaf(sv[e], scale_log2, nmb));
+  const float pmax = mx(mx(mx(pe[0], pe[1]), mx(pe[2], pe[3])), mx(mx(pe[4], pe[5]), mx(pe[6], pe[7])));
+  if (__builtin_amdgcn_ballot_w64(!(pmax <= ref.thr))) {
+    const float mloc =
+        scale_log2 * rows_max(mx(mx(mx(sv[0], sv[1]), mx(sv[2], sv[3])), mx(mx(sv[4], sv[5]), mx(sv[6], sv[7]))));
+    const bool move = mloc > st.m + kLazyLog2;  // -inf > -inf is false: a fully masked column stays
+    if (__builtin_amdgcn_ballot_w64(move)) {
+      const float m_new = move ? mloc : st.m;
+      const float alpha = move ? fast_exp2(st.m - m_new) : 1.f;
+      st.l *= alpha;
+#pragma unroll
+      for (int mm = 0; mm < kMM; ++mm) st.acc[mm] *= alpha;
+      st.m = m_new;
+    }
+    ref.set(st.m, real);
+    const float nmb2 = st.m == kNegInf ? 0.f : -st.m;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(__builtin_fmaf(sv[e], scale_log2, nmb2));
+  }
   st.l += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
   static_assert(kMM == 2 * N, "16-bit types: two head-dim rows per V word");
 
@@ -403,6 +427,7 @@ void attn_prefill_kernel(AttnParams prm) {
   };
 
   WaveState<kMM> st[kGW];
+  PairRef ref[kGW];
   // fp32 scales its logits directly.  16-bit types take |scale| (see above),
   // and a zero scale as the smallest normal float: every logit c * S is then
   // within 2^-24 of zero for |S| < 2^100, so every weight exp2(c * S - m)
@@ -461,7 +486,8 @@ void attn_prefill_kernel(AttnParams prm) {
           for (int g = 0; g < kGW; ++g) {
             const bool mask = (sub + 2) * kSub > vis_first[g];
             softmax_pv_pair<DT, N, kMM, kEx>(S[g][0], S[g][1], ve, vo, mask, valid_of(g, sub),
-                                             valid_of(g, sub + 1), scale_log2, r, st[g]);
+                                             valid_of(g, sub + 1), scale_log2, r, st[g], ref[g],
+                                             vis[g] > 0);
           }
         }
       }
@@ -494,7 +520,10 @@ void attn_prefill_kernel(AttnParams prm) {
   // the pace.)
   auto stream_context = [&](auto exact) {
 #pragma unroll
-    for (int g = 0; g < kGW; ++g) st[g].reset();
+    for (int g = 0; g < kGW; ++g) {
+      st[g].reset();
+      ref[g].set(kNegInf, vis[g] > 0);
+    }
     Tile<N> t;
     load_sub(t, st0 * kWaves + w);
     park(t, 0, exact);
