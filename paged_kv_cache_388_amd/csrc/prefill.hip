@@ -529,6 +529,23 @@ void attn_prefill_kernel(AttnParams prm) {
     park(t, 0, exact);
     __syncthreads();
     for (int sg = st0; sg < st1; ++sg) {
+      // With the contexts cut into parts every workgroup has the same work,
+      // and those sharing a compute unit otherwise progress at the issue
+      // arbiter's whim (the older waves first), the last then running alone;
+      // the waves with more of their part left go first, so that they keep
+      // pace.  (Uncut contexts differ in length and are dispatched longest
+      // first: there it made no difference or cost a little.)
+      if (P > 1) {
+        const int left = st1 - sg;
+        if (left > 48)
+          __builtin_amdgcn_s_setprio(3);
+        else if (left > 24)
+          __builtin_amdgcn_s_setprio(2);
+        else if (left > 8)
+          __builtin_amdgcn_s_setprio(1);
+        else
+          __builtin_amdgcn_s_setprio(0);
+      }
       load_sub(t, (sg + 1) * kWaves + w);
       compute_stage(sg, 0, exact);
       __syncthreads();  // every wave has read the stage
