@@ -566,6 +566,54 @@ def reread_rate(nbytes, rounds, steps, warmup):
     return n, ms, n * rounds / (ms * 1e-3) / 1e9
 
 
+def clock_summary(rec, multi):
+    """Summary of one call's clock records (pkv_clock_read: uint64 [n, 4]):
+    decode waves or prefill workgroups, times in microseconds from the
+    earliest start (the counter runs at 100 MHz)."""
+    rec = np.asarray(rec, dtype=np.uint64)
+    rec = rec[rec[:, 1] != 0]
+    t0 = rec[:, 0].astype(np.int64)
+    t1 = rec[:, 1].astype(np.int64)
+    base = t0.min()
+    start = (t0 - base) / 100.0
+    end = (t1 - base) / 100.0
+    xcd = (rec[:, 2] & np.uint64(0xff)).astype(np.int64)
+    r1 = lambda x: round(float(x), 1)
+    out = {"units": int(rec.shape[0]), "start_max_us": r1(start.max()),
+           "end_p50_us": r1(np.median(end)), "end_max_us": r1(end.max()),
+           "xcd_end_p50_us": [r1(np.median(end[xcd == x])) if (xcd == x).any() else None
+                              for x in range(8)],
+           "xcd_end_max_us": [r1(end[xcd == x].max()) if (xcd == x).any() else None
+                              for x in range(8)]}
+    if not multi:
+        pieces = (rec[:, 2] >> np.uint64(40)).astype(np.int64)
+        resid = np.zeros_like(end)
+        for x in range(8):
+            m = xcd == x
+            if m.any():
+                resid[m] = end[m] - np.median(end[m])
+        out.update({"within_xcd_p10_us": r1(np.percentile(resid, 10)),
+                    "within_xcd_p90_us": r1(np.percentile(resid, 90)),
+                    "pieces_mean": round(float(pieces.mean()), 2),
+                    "corr_end_pieces_within_xcd":
+                        round(float(np.corrcoef(resid, pieces)[0, 1]), 3) if pieces.std() > 0 else None})
+    else:
+        seq = ((rec[:, 2] >> np.uint64(8)) & np.uint64(0xffffff)).astype(np.int64)
+        stages = (rec[:, 3] & np.uint64(0xfffff)).astype(np.int64)
+        ctx = (rec[:, 3] >> np.uint64(32)).astype(np.int64)
+        per_seq = []
+        for sv in np.unique(seq):
+            m = seq == sv
+            per_seq.append({"seq": int(sv), "context": int(ctx[m][0]), "workgroups": int(m.sum()),
+                            "start_p50_us": r1(np.median(start[m])), "end_max_us": r1(end[m].max()),
+                            "us_per_stage_p50": round(float(np.median((end[m] - start[m]) /
+                                                                      np.maximum(stages[m], 1))), 3)})
+        ts = np.linspace(0.0, float(end.max()), 11)
+        out.update({"sequences": per_seq,
+                    "running_at_tenths": [int(((start <= t) & (end > t)).sum()) for t in ts]})
+    return out
+
+
 def reread_probe(mib, rounds, steps, warmup):
     """Print the re-read probe's rate for a buffer of `mib` MiB."""
     n, ms, gbs = reread_rate(mib * (1 << 20), rounds, steps, warmup)
@@ -617,6 +665,11 @@ def main():
     ap.add_argument("--block-manager", action="store_true",
                     help="instead of the decode step, time the host block manager on a "
                          "serving-style trace")
+    ap.add_argument("--clock", action="store_true",
+                    help="after the warmup, run --steps attention calls of the clock build "
+                         "(PAGEDKV_CLOCK=1; bf16, D 128, 16-token blocks) and print each "
+                         "call's per-wave (decode) or per-workgroup (prefill) start/end "
+                         "summary instead of the bench line")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the decode step, time pkv_stream_copy of this many MiB "
                          "(the reference copy for bandwidth and HBM counter calibration)")
@@ -715,6 +768,22 @@ def main():
         write_step()
         attend()
     torch.cuda.synchronize()
+
+    if args.clock:
+        if w.dtype != "bf16" or w.head_dim != 128 or w.block_size != 16:
+            print("--clock: the clock build exists for bf16, head_dim 128, 16-token blocks only",
+                  file=sys.stderr)
+            sys.exit(2)
+        calls = []
+        for i in range(args.steps):
+            os.environ["PAGEDKV_CLOCK"] = "1"
+            attend()
+            del os.environ["PAGEDKV_CLOCK"]
+            calls.append(clock_summary(_lib.pkv_clock_read(), w.multi))
+            print(f"[bench] clock call {i}: last end {calls[-1]['end_max_us']} us",
+                  file=sys.stderr, flush=True)
+        print(json.dumps({"clock": w.name, "calls": calls}))
+        return
 
     stream = torch.cuda.current_stream()
     scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold else None

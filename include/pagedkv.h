@@ -372,6 +372,30 @@ PKV_API pkv_status pkv_stream_read(const void* src, size_t bytes, uint32_t* sink
 PKV_API pkv_status pkv_stream_reread(const void* src, size_t bytes, int32_t rounds,
                                      uint32_t* sink, hipStream_t stream);
 
+/*
+ * Clock records — measurement only, not part of the attention method.  With
+ * PAGEDKV_CLOCK=1 in the environment (read on every call), an attention call
+ * on a bf16 pool with head_dim 128 and 16-token blocks, not under graph
+ * capture, runs a build of its kernels that also records, per stream-decode
+ * wave (record index = wave of the grid) or per prefill workgroup that
+ * streams a context (record index = linear block id), 4 words:
+ *   [0] the real-time counter (100 MHz) at its start, [1] at its end,
+ *   [2] bits 0-7 the XCD it ran on; decode: bits 8-39 its positions (kv head
+ *       x 16-token sub-tile), bits 40-63 the pieces it finished; prefill:
+ *       bits 8-31 the sequence, 32-47 the kv head, 48-63 the column block,
+ *   [3] decode: its workgroup (in the order positions are dealt); prefill:
+ *       bits 0-19 the stages (64 tokens) it streamed, 20-31 its part of the
+ *       context, 32-63 the context length.
+ * Outputs are those of the normal kernels bit for bit.  The records live in
+ * a library-held array per GPU (pkv_clock_records() records), cleared on the
+ * call's stream before each such call; records not written read as zeros.
+ * pkv_clock_read waits for all work on the current device, then copies the
+ * first `records` records into host (records * 4 uint64); PKV_EINVAL if more
+ * than pkv_clock_records() are asked for.
+ */
+PKV_API int32_t pkv_clock_records(void);
+PKV_API pkv_status pkv_clock_read(unsigned long long* host, size_t records);
+
 /* ------------------------------------------------------------------------
  * Host block manager (host memory only; no device work).
  *

@@ -75,6 +75,10 @@ def load():
     lib.pkv_stream_read.restype = c_i32
     lib.pkv_stream_reread.argtypes = [c_vp, c_sz, c_i32, c_vp, c_vp]
     lib.pkv_stream_reread.restype = c_i32
+    lib.pkv_clock_records.argtypes = []
+    lib.pkv_clock_records.restype = c_i32
+    lib.pkv_clock_read.argtypes = [c_vp, c_sz]
+    lib.pkv_clock_read.restype = c_i32
     lib.pkv_status_string.argtypes = [c_i32]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_last_error.argtypes = []
@@ -354,6 +358,18 @@ def pkv_stream_reread(src, rounds, sink, stream=None):
         raise ValueError("sink must hold 2048 32-bit words")
     _check(load().pkv_stream_reread(_ptr(src), src.numel() * src.element_size(), int(rounds),
                                     _ptr(sink), _stream(stream)))
+
+
+def pkv_clock_read(records=None):
+    """The clock records of the last attention call made with
+    PAGEDKV_CLOCK=1 on the current device (waits for the device): a uint64
+    array [records, 4], zeros where nothing was recorded."""
+    import numpy as np
+    lib = load()
+    n = lib.pkv_clock_records() if records is None else int(records)
+    buf = np.zeros((max(n, 0), 4), dtype=np.uint64)
+    _check(lib.pkv_clock_read(buf.ctypes.data_as(ctypes.c_void_p), n))
+    return buf
 
 
 # ---------------------------------------------------------------------------

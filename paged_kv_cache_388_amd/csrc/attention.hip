@@ -386,9 +386,15 @@ __device__ __forceinline__ int group_rows(const SeqCols& sc, int cg, int G, int 
   return v > kSub ? kSub : v;
 }
 
-template <int DT, int D, int BS, bool MULTI, bool KDIRECT = false>
+// kClock: the measurement build, which also records each wave's start and
+// end (see clock_record; word 2 adds the wave's positions and the pieces it
+// finished, word 3 its workgroup as numbered by xcd_remap).
+template <int DT, int D, int BS, bool MULTI, bool KDIRECT = false, bool kClock = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_stream_kernel(AttnParams prm) {
+  [[maybe_unused]] unsigned long long clk0 = 0;
+  [[maybe_unused]] int clk_pieces = 0;
+  if constexpr (kClock) clk0 = clock_now();
   using Geo = Geometry<DT, D, BS>;
   constexpr int N = Geo::N;
   constexpr int kMM = Geo::kMM;
@@ -651,6 +657,7 @@ void attn_stream_kernel(AttnParams prm) {
     valid = valid > kSub ? kSub : valid;
     attend_subtile<DT, N, kMM, KDIRECT>(t, qb, valid, scale_log2, r, st, kst);
     if (m.p + 1 == sc.E || m.p + 1 == b) {
+      if constexpr (kClock) ++clk_pieces;
       finish_piece(m.p + 1);
       open = false;
     }
@@ -761,6 +768,10 @@ void attn_stream_kernel(AttnParams prm) {
     const float2 ml = own_state(1, o);
     finish_span(o, ml.x, ml.y, 1);
   }
+  if constexpr (kClock)
+    if (lane == 0)
+      clock_record(prm.clock, wv, clk0, (unsigned long long)(b - a) | ((unsigned long long)clk_pieces << 32),
+                   (unsigned long long)wg);
 }
 
 // Merge of the pieces of one split (sequence, kv head, column group) for one
@@ -948,10 +959,14 @@ hipError_t launch_typed(const AttnParams& prm, hipStream_t stream) {
                            0, stream, prm);
       return hipGetLastError();
     }
-    // K loaded straight in the MFMA operand order: a measurement variant,
-    // built for one shape only (bf16, D 128, 16-token blocks)
+    // K loaded straight in the MFMA operand order, and the clock build: two
+    // measurement variants, built for one shape only (bf16, D 128, 16-token
+    // blocks)
     constexpr bool kDirectBuilt = DT == DT_BF16 && D == 128 && BS == 16;
-    if (prm.k_direct && kDirectBuilt)
+    if (prm.clock && kDirectBuilt)
+      hipLaunchKernelGGL((attn_stream_kernel<DT, D, BS, false, false, kDirectBuilt>),
+                         dim3((unsigned)prm.stream_wgs), block, 0, stream, prm);
+    else if (prm.k_direct && kDirectBuilt)
       hipLaunchKernelGGL((attn_stream_kernel<DT, D, BS, false, kDirectBuilt>),
                          dim3((unsigned)prm.stream_wgs), block, 0, stream, prm);
     else

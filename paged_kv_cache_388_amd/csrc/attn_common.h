@@ -416,5 +416,27 @@ __device__ __forceinline__ void load_run(const float* src, float (&o)[D / 4]) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The clock builds' record: the real-time counter (100 MHz) at the start and
+// at the end, the XCD the wave ran on (hardware register XCC_ID) in the low
+// byte of word 2, and what the kernel adds to words 2 and 3.
+__device__ __forceinline__ unsigned long long clock_now() { return __builtin_amdgcn_s_memrealtime(); }
+
+__device__ __forceinline__ unsigned xcd_id() {
+  unsigned x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return x & 0xffu;
+}
+
+__device__ __forceinline__ void clock_record(unsigned long long* rec, long long index,
+                                             unsigned long long t0, unsigned long long w2,
+                                             unsigned long long w3) {
+  if (index < 0 || index >= kClockRecords) return;
+  unsigned long long* r = rec + index * kClockWords;
+  r[0] = t0;
+  r[1] = clock_now();
+  r[2] = (unsigned long long)xcd_id() | (w2 << 8);
+  r[3] = w3;
+}
+
 }  // namespace
 }  // namespace pkv

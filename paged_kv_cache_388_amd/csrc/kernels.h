@@ -98,7 +98,15 @@ struct AttnParams {
   // the MFMA operand order instead of whole lines re-dealt through LDS
   // (built for bf16, D 128, 16-token blocks only; ignored elsewhere).
   int32_t k_direct;
+  // Measurement only: when non-null, the clock build of the kernel (bf16,
+  // D 128, 16-token blocks) records kClockWords words per wave (stream
+  // decode: record wave index) or per workgroup (prefill: record linear
+  // block id), up to kClockRecords records; see pkv_clock_read.
+  unsigned long long* clock;
 };
+
+constexpr int kClockRecords = 32768;
+constexpr int kClockWords = 4;
 
 // Workspace layout of one decode call, shared by the size query and the call.
 struct AttnWorkspace {

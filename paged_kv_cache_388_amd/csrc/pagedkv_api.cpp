@@ -140,6 +140,35 @@ bool k_direct_loads() {
   return v && strcmp(v, "direct") == 0;
 }
 
+// ---- clock records (measurement) -------------------------------------------
+// PAGEDKV_CLOCK=1 in the environment: attention calls of the shape the clock
+// builds exist for (bf16, D 128, 16-token blocks) run them, which record each
+// decode wave's or prefill workgroup's start, end and XCD into this array
+// (one per GPU, held until the process ends; cleared on the call's stream
+// first).  pkv_clock_read copies it out.  Calls under graph capture, and
+// calls of other shapes, run the normal kernels.  Read on every call.
+constexpr size_t kClockBytes = (size_t)pkv::kClockRecords * pkv::kClockWords * sizeof(unsigned long long);
+static __device__ __align__(256) unsigned long long clock_records[pkv::kClockRecords * pkv::kClockWords];
+
+bool clock_mode() {
+  const char* v = getenv("PAGEDKV_CLOCK");
+  return v && v[0] == '1' && v[1] == '\0';
+}
+
+// Device address of this GPU's record array (looked up once per device with
+// that device current), or nullptr.
+unsigned long long* clock_on_current_device() {
+  static std::atomic<void*> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = cached[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(clock_records)) != hipSuccess) return nullptr;
+    cached[dev].store(ptr, std::memory_order_release);
+  }
+  return static_cast<unsigned long long*>(ptr);
+}
+
 // Workgroups of the stream path for this call on the current device, or 0
 // where it cannot take the call: a batch above its LDS tables, or more
 // positions (kv heads x column groups x sub-tiles) than it indexes.  Decode
@@ -381,6 +410,14 @@ pkv_status attention_call(const char* what, void* out, const void* q, const void
   prm.prefill_parts = pf_parts;
   prm.prefill_wave_groups = plan.wave_groups;
   prm.k_direct = !multi && k_direct_loads() ? 1 : 0;
+  prm.clock = nullptr;
+  if (clock_mode()) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone) {
+      unsigned long long* rec = clock_on_current_device();
+      if (rec && hipMemsetAsync(rec, 0, kClockBytes, stream) == hipSuccess) prm.clock = rec;
+    }
+  }
   hipError_t err = pkv::launch_paged_attention(prm, pool.dtype, pool.head_dim, pool.block_size, stream);
   return err == hipSuccess ? PKV_OK : hip_fail(err, what);
 }
@@ -454,6 +491,24 @@ void* scratch_on_current_device() {
 extern "C" {
 
 size_t paged_attention_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int32_t pkv_clock_records(void) { return pkv::kClockRecords; }
+
+pkv_status pkv_clock_read(unsigned long long* host, size_t records) {
+  g_err[0] = '\0';
+  if (records > (size_t)pkv::kClockRecords)
+    return fail(PKV_EINVAL, "pkv_clock_read: %zu records asked for, %d held", records,
+                pkv::kClockRecords);
+  if (records == 0) return PKV_OK;
+  if (!host) return fail(PKV_EINVAL, "pkv_clock_read: null host buffer");
+  unsigned long long* rec = clock_on_current_device();
+  if (!rec) return fail(PKV_EHIP, "pkv_clock_read: record array not found on this device");
+  hipError_t err = hipDeviceSynchronize();
+  if (err == hipSuccess)
+    err = hipMemcpy(host, rec, records * pkv::kClockWords * sizeof(unsigned long long),
+                    hipMemcpyDeviceToHost);
+  return err == hipSuccess ? PKV_OK : hip_fail(err, "pkv_clock_read");
+}
 
 pkv_status paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache,
                                           const void* v_cache, pkv_pool pool,

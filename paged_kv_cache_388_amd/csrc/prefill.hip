@@ -217,9 +217,14 @@ __device__ __forceinline__ void softmax_pv_pair(const floatx4& S0, const floatx4
 // parts' states.  Grid: (column block, part) x kv head x sequence rank;
 // blocks past a sequence's columns, and empty parts, exit at once.
 
-template <int DT, int D, int BS, int GW>
+// kClock: the measurement build, which also records each workgroup that
+// streams a context (see clock_record; word 2 adds the sequence, kv head and
+// column block, word 3 the part's stages, the part and the context length).
+template <int DT, int D, int BS, int GW, bool kClock = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GW == 2 ? 2 : 3)))
 void attn_prefill_kernel(AttnParams prm) {
+  [[maybe_unused]] unsigned long long clk0 = 0;
+  if constexpr (kClock) clk0 = clock_now();
   static_assert(GW == 1 || (GW == 2 && DT != DT_F32), "two groups per wave: 16-bit types");
   using Geo = Geometry<DT, D, BS>;
   constexpr int N = Geo::N;
@@ -572,6 +577,13 @@ void attn_prefill_kernel(AttnParams prm) {
   }
 
 
+  if constexpr (kClock)
+    if (tid == 0)
+      clock_record(prm.clock,
+                   (long long)blockIdx.x + (long long)gridDim.x * (blockIdx.y + (long long)gridDim.y * blockIdx.z),
+                   clk0, (unsigned long long)s | ((unsigned long long)h << 24) | ((unsigned long long)cb << 40),
+                   (unsigned long long)(st1 - st0) | ((unsigned long long)part << 20) |
+                       ((unsigned long long)n << 32));
 #pragma unroll
   for (int g = 0; g < kGW; ++g) {
     if (cg0 + g >= ngrp) break;
@@ -718,12 +730,23 @@ hipError_t launch_prefill_typed(const AttnParams& prm, hipStream_t stream) {
         prm.prefill_parts < 1 || nx > 0x7fffffffLL)
       return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)nx, (unsigned)prm.num_kv_heads, (unsigned)prm.num_seqs);
-    if (prm.prefill_wave_groups == 1)
-      hipLaunchKernelGGL((attn_prefill_kernel<DT, D, BS, 1>), grid, block, 0, stream, prm);
-    else if constexpr (DT != DT_F32)
-      hipLaunchKernelGGL((attn_prefill_kernel<DT, D, BS, 2>), grid, block, 0, stream, prm);
-    else
+    // the clock build: a measurement variant of one shape (bf16, D 128,
+    // 16-token blocks)
+    constexpr bool kClockBuilt = DT == DT_BF16 && D == 128 && BS == 16;
+    const bool clock = prm.clock != nullptr && kClockBuilt;
+    if (prm.prefill_wave_groups == 1) {
+      if (clock)
+        hipLaunchKernelGGL((attn_prefill_kernel<DT, D, BS, 1, kClockBuilt>), grid, block, 0, stream, prm);
+      else
+        hipLaunchKernelGGL((attn_prefill_kernel<DT, D, BS, 1>), grid, block, 0, stream, prm);
+    } else if constexpr (DT != DT_F32) {
+      if (clock)
+        hipLaunchKernelGGL((attn_prefill_kernel<DT, D, BS, 2, kClockBuilt>), grid, block, 0, stream, prm);
+      else
+        hipLaunchKernelGGL((attn_prefill_kernel<DT, D, BS, 2>), grid, block, 0, stream, prm);
+    } else {
       return hipErrorInvalidValue;
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || prm.prefill_parts == 1) return err;
     const long long threads =

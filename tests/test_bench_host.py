@@ -96,3 +96,36 @@ def test_shared_block_bytes_by_hand():
     assert reads == 4
     assert sb == 2 * 6 * 16 * w.num_kv_heads * w.head_dim * 2
     assert bench.shared_block_bytes(wl.tiny_f32()) == (0, 0.0)
+
+
+def test_clock_summary_by_hand():
+    """bench.py --clock: per-XCD end times, the within-XCD spread and the
+    per-sequence prefill figures from hand-made records (100 MHz counter)."""
+    def rec(start, end, w2, w3):
+        return [start, end, w2, w3]
+    # decode: two waves per XCD, ending at 100 + 10 x and 104 + 10 x us
+    rows = []
+    for x in range(8):
+        for k, extra in enumerate((0, 4)):
+            pieces = 1 + k
+            rows.append(rec(1000, 1000 + (100 + 10 * x + extra) * 100, x | (50 << 8) | (pieces << 40), 0))
+    rows.append(rec(0, 0, 0, 0))  # an unwritten record is skipped
+    s = bench.clock_summary(np.array(rows, dtype=np.uint64), multi=False)
+    assert s["units"] == 16
+    assert s["end_max_us"] == 174.0
+    assert s["xcd_end_p50_us"] == [102.0 + 10 * x for x in range(8)]
+    assert s["xcd_end_max_us"] == [104.0 + 10 * x for x in range(8)]
+    assert s["within_xcd_p10_us"] == -2.0 and s["within_xcd_p90_us"] == 2.0
+    assert s["pieces_mean"] == 1.5 and s["corr_end_pieces_within_xcd"] == 1.0
+    # prefill: sequence 3 (context 640, 10 stages) on two workgroups, sequence 5 on one
+    rows = [rec(0, 2000, 0 | (3 << 8), 10 | (640 << 32)),
+            rec(100, 2100, 1 | (3 << 8), 10 | (640 << 32)),
+            rec(500, 1500, 2 | (5 << 8), 4 | (1 << 20) | (256 << 32))]
+    s = bench.clock_summary(np.array(rows, dtype=np.uint64), multi=True)
+    assert s["units"] == 3 and s["end_max_us"] == 21.0
+    assert s["sequences"] == [
+        {"seq": 3, "context": 640, "workgroups": 2, "start_p50_us": 0.5, "end_max_us": 21.0,
+         "us_per_stage_p50": 2.0},
+        {"seq": 5, "context": 256, "workgroups": 1, "start_p50_us": 5.0, "end_max_us": 15.0,
+         "us_per_stage_p50": 2.5}]
+    assert s["running_at_tenths"][0] == 1 and s["running_at_tenths"][-1] == 0
