@@ -57,3 +57,13 @@ def test_prefill_clock_build(monkeypatch):
     assert set(seq.tolist()) == {0, 1, 2}
     for s in (0, 1, 2):
         assert np.all(ctx_rec[seq == s] == ctx[s])
+
+
+def test_clock_ignored_for_other_shapes(monkeypatch):
+    """PAGEDKV_CLOCK=1 on a shape without a clock build (fp16) runs the
+    normal kernels: same output, no records."""
+    rng = np.random.default_rng(63)
+    w = wl.build("clock_f16", 63, rng, [5, 300, 1000], 8, 2, 128, 16, "f16")
+    print(f"[gpu] clock switch on an fp16 pool: B={w.num_seqs}", flush=True)
+    rec = _both(w, monkeypatch)
+    assert rec.shape[0] == 0
