@@ -156,9 +156,12 @@ def test_too_many_sequences_refused():
         dw.attend()
 
 
-@pytest.mark.parametrize("name", ["spec_verify", "prefill_chunk"])
+@pytest.mark.parametrize("name", ["spec_verify", "prefill_chunk", "long_prompt_chunk"])
 def test_full_size_multi_workloads(name):
-    w = wl.named(name)
+    """Every row of the full-size multi-token workloads (the long prompt's
+    context cut into parts and merged) against the oracle, on NaN-poisoned
+    pools."""
+    w = wl.named(name, poison=True)
     err = _run(w, name)
     print(f"[gpu] {name}: max |gpu - oracle| = {err:.3e}", flush=True)
 
