@@ -140,3 +140,15 @@ def test_noalloc_refuses_calls_beyond_its_scratch(lib):
     assert call(FAKE, FAKE, FAKE, FAKE, p, FAKE, 4, FAKE, 2, 3, 0.1, 64, None) == 1  # H_q % H_kv
     assert call(FAKE, FAKE, FAKE, FAKE, p, FAKE, 3, FAKE, 2, 2, 0.1, 64, None) == 1  # table too short
     assert call(None, None, None, None, p, None, 0, None, 0, 2, 0.1, 0, None) == 0   # empty batch
+
+
+def test_clock_read_arguments(lib):
+    """pkv_clock_read refuses more records than the library holds, and an
+    empty read succeeds, both before any device call."""
+    n = lib.pkv_clock_records()
+    assert n == 32768
+    buf = (ctypes.c_ulonglong * 4)()
+    assert lib.pkv_clock_read(buf, n + 1) == 1
+    assert b"records asked for" in lib.pkv_last_error()
+    assert lib.pkv_clock_read(None, 0) == 0
+    assert lib.pkv_clock_read(None, 1) == 1
